@@ -1,0 +1,192 @@
+"""fp64 oracle of the fused linear + cross-entropy (FLCE) loss head.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and ``bench.py``'s ``cpu_baseline`` leg, never by the product path.
+
+What is computed, and where the pages state it
+-----------------------------------------------
+* Page 2, "Liger-Kernel: Triton kernels that replace Hugging Face training
+  ops", section "What actually gets replaced, and how the patch mechanism
+  works": the fused head takes the hidden states and the LM-head weight and
+  returns the loss itself; the (batch, sequence, vocab) logits are never
+  materialised.
+* Page 3, "Complete Guide to Liger Kernel", section
+  "LigerFusedLinearCrossEntropyLoss": the call is (hidden [B*S, H],
+  weight [V, H], labels [B*S]) -> scalar loss; section "LigerCrossEntropyLoss":
+  the loss is the cross entropy of the logits against the labels.
+* Page 1, "Liger Kernel explained", section "What does Liger Kernel actually
+  fuse, and why does that cut memory?": the fused kernel produces the loss
+  and its gradient together, working through the logits in chunks, so that
+  chunking only changes the order of accumulation (the same page's
+  measurement table asks for a numerical parity check for that reason).
+
+The result has a plain definition, so this module writes it out:
+
+    Z      = h W^T                                  logits        [N, V]
+    lse_i  = m_i + ln sum_j exp(Z_ij - m_i),  m_i = max_j Z_ij
+    loss   = (1/N) sum_i (lse_i - Z_{i, t_i})       mean over all N tokens
+    G      = (softmax(Z) - onehot(t)) / N           dloss/dZ      [N, V]
+    grad_h = G W                                    dloss/dh      [N, H]
+    grad_W = G^T h                                  dloss/dW      [V, H]
+
+Readings where the pages are silent (each is listed in the design notes):
+the reduction is the mean over all N tokens (a bare cross-entropy call);
+every target is a valid class (no ignore index); there is no bias, label
+smoothing, z-loss, soft-capping or temperature; h is [N, H] and W is [V, H],
+row-major.
+
+Three implementations, all fp64:
+* ``flce``          the definition above, unchunked (small inputs);
+* ``flce_chunked``  the same steps over token chunks, grad_W accumulated in
+                    fp64 and the 1/N taken with the global N (any size);
+* ``flce_brute``    pure-Python loops (tiny inputs; pins numpy's matmul and
+                    broadcasting);
+and ``flce_sampled`` for full-size checks: the loss plus chosen rows of
+grad_h and grad_W, without holding an [N, V] or [V, H] array.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _check(h: np.ndarray, W: np.ndarray, t: np.ndarray) -> None:
+    if h.ndim != 2 or W.ndim != 2 or t.ndim != 1:
+        raise ValueError("expected h[N,H], W[V,H], t[N]")
+    if h.shape[1] != W.shape[1] or h.shape[0] != t.shape[0]:
+        raise ValueError("shape mismatch")
+    if h.shape[0] < 1:
+        raise ValueError("N must be >= 1: the mean over no tokens is undefined")
+    if t.size and (t.min() < 0 or t.max() >= W.shape[0]):
+        raise ValueError("targets must lie in [0, V)")
+
+
+def logits(h: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Z = h W^T in fp64 (the LM-head linear layer, no bias)."""
+    return np.asarray(h, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T
+
+
+def logsumexp_rows(Z: np.ndarray) -> np.ndarray:
+    """Per-row log-sum-exp, shifted by the row maximum so exp never overflows."""
+    m = Z.max(axis=1)
+    return m + np.log(np.exp(Z - m[:, None]).sum(axis=1))
+
+
+def row_losses(Z: np.ndarray, t: np.ndarray) -> np.ndarray:
+    """Cross entropy of each row: lse_i - Z[i, t_i]."""
+    return logsumexp_rows(Z) - Z[np.arange(Z.shape[0]), t]
+
+
+def dlogits(Z: np.ndarray, t: np.ndarray, n_total: int) -> np.ndarray:
+    """dloss/dZ for the mean loss over n_total tokens: (softmax - onehot)/N."""
+    P = np.exp(Z - logsumexp_rows(Z)[:, None])
+    P[np.arange(Z.shape[0]), t] -= 1.0
+    return P / n_total
+
+
+def flce(h: np.ndarray, W: np.ndarray, t: np.ndarray):
+    """Unchunked definition: returns (loss, grad_h, grad_W) in fp64."""
+    h = np.asarray(h, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    t = np.asarray(t, dtype=np.int64)
+    _check(h, W, t)
+    N = h.shape[0]
+    Z = logits(h, W)
+    loss = row_losses(Z, t).sum() / N
+    G = dlogits(Z, t, N)
+    return float(loss), G @ W, G.T @ h
+
+
+def flce_chunked(h: np.ndarray, W: np.ndarray, t: np.ndarray, chunk: int):
+    """The same result computed over token chunks of ``chunk`` rows.
+
+    Only a [chunk, V] block of logits exists at a time.  grad_W sums the
+    chunks' contributions in fp64; every chunk divides by the global N.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    t = np.asarray(t, dtype=np.int64)
+    _check(h, W, t)
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    N = h.shape[0]
+    loss_sum = 0.0
+    grad_h = np.empty_like(h)
+    grad_W = np.zeros_like(W)
+    for r0 in range(0, N, chunk):
+        r1 = min(N, r0 + chunk)
+        Z = logits(h[r0:r1], W)
+        loss_sum += row_losses(Z, t[r0:r1]).sum()
+        G = dlogits(Z, t[r0:r1], N)
+        grad_h[r0:r1] = G @ W
+        grad_W += G.T @ h[r0:r1]
+    return float(loss_sum / N), grad_h, grad_W
+
+
+def flce_brute(h, W, t):
+    """Pure-Python loops over the definition (tiny inputs only)."""
+    h = [[float(x) for x in row] for row in np.asarray(h, dtype=np.float64)]
+    W = [[float(x) for x in row] for row in np.asarray(W, dtype=np.float64)]
+    t = [int(x) for x in np.asarray(t)]
+    N, H, V = len(h), len(W[0]), len(W)
+    if N < 1:
+        raise ValueError("N must be >= 1")
+    loss = 0.0
+    G = [[0.0] * V for _ in range(N)]
+    for i in range(N):
+        z = [sum(h[i][k] * W[j][k] for k in range(H)) for j in range(V)]
+        m = max(z)
+        s = sum(math.exp(zj - m) for zj in z)
+        lse = m + math.log(s)
+        loss += lse - z[t[i]]
+        for j in range(V):
+            G[i][j] = (math.exp(z[j] - lse) - (1.0 if j == t[i] else 0.0)) / N
+    grad_h = [[sum(G[i][j] * W[j][k] for j in range(V)) for k in range(H)]
+              for i in range(N)]
+    grad_W = [[sum(G[i][j] * h[i][k] for i in range(N)) for k in range(H)]
+              for j in range(V)]
+    return loss / N, np.array(grad_h), np.array(grad_W)
+
+
+def flce_sampled(h, W, t, rows=(), vocab_rows=(), chunk: int = 1024):
+    """Loss, per-row lse and chosen rows of grad_h / grad_W at any size.
+
+    Streams over token chunks; holds at most a [chunk, V] logit block plus
+    the requested rows.  Returns a dict with ``loss`` (float), ``lse`` [N],
+    ``row_loss`` [N], ``grad_h_rows`` [len(rows), H] and ``grad_W_rows``
+    [len(vocab_rows), H].
+    """
+    h = np.asarray(h, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    t = np.asarray(t, dtype=np.int64)
+    _check(h, W, t)
+    N, H = h.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    vocab_rows = np.asarray(vocab_rows, dtype=np.int64)
+    lse = np.empty(N)
+    row_loss = np.empty(N)
+    gh = np.zeros((rows.size, H))
+    gw = np.zeros((vocab_rows.size, H))
+    for r0 in range(0, N, chunk):
+        r1 = min(N, r0 + chunk)
+        Z = logits(h[r0:r1], W)
+        lse[r0:r1] = logsumexp_rows(Z)
+        row_loss[r0:r1] = lse[r0:r1] - Z[np.arange(r1 - r0), t[r0:r1]]
+        sel = np.nonzero((rows >= r0) & (rows < r1))[0]
+        if sel.size:
+            G = dlogits(Z[rows[sel] - r0], t[rows[sel]], N)
+            gh[sel] = G @ W
+        if vocab_rows.size:
+            P = np.exp(Z[:, vocab_rows] - lse[r0:r1, None])
+            P -= (t[r0:r1, None] == vocab_rows[None, :])
+            gw += (P / N).T @ h[r0:r1]
+        del Z
+    return {
+        "loss": float(row_loss.sum() / N),
+        "lse": lse,
+        "row_loss": row_loss,
+        "grad_h_rows": gh,
+        "grad_W_rows": gw,
+    }
