@@ -1,0 +1,129 @@
+/*
+ * flce.h - fused linear + cross-entropy loss head for AMD Instinct MI355X
+ * (CDNA4, gfx950): C ABI.
+ *
+ * The operation (page 2, "Liger-Kernel: Triton kernels that replace Hugging
+ * Face training ops", section "What actually gets replaced, and how the patch
+ * mechanism works"; page 3, "Complete Guide to Liger Kernel", section
+ * "LigerFusedLinearCrossEntropyLoss"): given hidden states h[N,H], the
+ * LM-head weight W[V,H] and class labels t[N], return the cross-entropy loss
+ * of the logits h W^T directly, without a [N,V] logit tensor, together with
+ * its gradients (page 1, "Liger Kernel explained", section "What does Liger
+ * Kernel actually fuse, and why does that cut memory?": loss and gradient
+ * are produced in the same pass, working through the logits in chunks).
+ *
+ *   Z      = h W^T                                   (never resident whole)
+ *   loss   = (1/N) sum_i ( logsumexp_j Z_ij - Z_{i,t_i} )
+ *   G      = (softmax(Z) - onehot(t)) / N
+ *   grad_h = G W,     grad_W = G^T h
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer is a DEVICE pointer unless stated otherwise; arrays are
+ *    row-major and contiguous; the caller allocates and owns every buffer.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL is the legacy default
+ *    stream).  No call synchronises, allocates device memory, or reads
+ *    device data on the host; results are valid once the stream has
+ *    completed.  Calls on different streams are independent when their
+ *    output and workspace buffers are distinct.
+ *  - Arguments are checked on the host before anything is enqueued; a
+ *    failed check returns a status and enqueues nothing.
+ *  - Requirements: H % 8 == 0 and 16-byte aligned h, W, grad_h, grad_W and
+ *    workspace (FLCE_ERR_UNSUPPORTED otherwise); all sizes below 2^31 and
+ *    N, H, V, chunk >= 1 (FLCE_ERR_INVALID_ARG otherwise).
+ *  - Targets must lie in [0, V).  An out-of-range target is not read
+ *    through: it makes that token's loss, and so the returned loss, NaN.
+ */
+#ifndef FLCE_H_
+#define FLCE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of h, W and grad_h.  grad_W and the loss are always fp32. */
+typedef enum flce_dtype {
+  FLCE_BF16 = 0, /* bfloat16: MFMA contractions, fp32 accumulation      */
+  FLCE_F32 = 1   /* float32 operands and fp32 gradient of the logits    */
+} flce_dtype;
+
+typedef enum flce_status {
+  FLCE_OK = 0,
+  FLCE_ERR_INVALID_ARG = 1, /* null pointer, size < 1 or >= 2^31, bad dtype */
+  FLCE_ERR_WORKSPACE = 2,   /* workspace smaller than flce_workspace_bytes   */
+  FLCE_ERR_UNSUPPORTED = 3, /* H % 8 != 0 or a pointer not 16-byte aligned   */
+  FLCE_ERR_HIP = 4          /* the HIP runtime reported a launch error       */
+} flce_status;
+
+/*
+ * Bytes of device workspace flce_fwd_bwd needs: min(chunk, N) * V * 4, the
+ * fp32 logits of one token chunk (the logits of all N tokens would take
+ * N * V * 4).  Returns 0 when a size is < 1.  Pure host function.
+ */
+size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk,
+                            flce_dtype dt);
+
+/*
+ * Forward and backward of the fused head in one call.
+ *
+ *  h          [N, H]  dt     hidden states (read only)
+ *  W          [V, H]  dt     LM-head weight, nn.Linear layout (read only)
+ *  targets    [N]     int32  class of each token, 0 <= t < V (read only)
+ *  chunk             tokens whose logits are live at once (clamped to N)
+ *  loss       [1]     fp32   overwritten with the mean token loss
+ *  grad_h     [N, H]  dt     overwritten with dloss/dh
+ *  grad_W     [V, H]  fp32   overwritten with dloss/dW (fp32 accumulation
+ *                            over token chunks)
+ *  workspace                 >= flce_workspace_bytes(N, H, V, chunk, dt)
+ *                            bytes of scratch, contents undefined on return
+ *
+ * The gradients are those of the mean loss with an upstream gradient of 1.
+ * Outputs must not alias inputs, the workspace or each other.
+ * Returns FLCE_OK once everything is enqueued.
+ */
+flce_status flce_fwd_bwd(const void* h, const void* W, const int32_t* targets,
+                         int64_t N, int64_t H, int64_t V, int64_t chunk,
+                         float* loss, void* grad_h, float* grad_W,
+                         void* workspace, size_t workspace_bytes,
+                         flce_dtype dt, hipStream_t stream);
+
+/*
+ * Step 1 alone: the logits of `rows` tokens, z[i * ldz + j] = sum_k
+ * h[i, k] W[j, k] in fp32 (MFMA, fp32 accumulation), for 0 <= i < rows,
+ * 0 <= j < V.  ldz >= V, in floats; z must be 16-byte aligned and, for the
+ * vectorised path, ldz % 4 == 0.  Same alignment rules as flce_fwd_bwd.
+ */
+flce_status flce_logits(const void* h, const void* W, int64_t rows, int64_t H,
+                        int64_t V, float* z, int64_t ldz, flce_dtype dt,
+                        hipStream_t stream);
+
+/*
+ * Steps 2-3 alone, on given fp32 logits (cross entropy with the gradient
+ * written in place, page 3 section "LigerCrossEntropyLoss"): for each of
+ * `rows` rows of z (pitch ldz floats, ldz >= V), computes
+ *   row_loss[i] = logsumexp_j z[i, j] - z[i, t_i]
+ * and rewrites the row in place as
+ *   G[i, j] = (exp(z[i, j] - lse_i) - [j == t_i]) * scale,
+ * stored as dt: for FLCE_F32 at the same positions; for FLCE_BF16 as bf16
+ * (round to nearest even) at element offset i * 2 * ldz + j of
+ * (uint16_t*)z, i.e. in the first half of the row's own bytes.
+ * row_loss [rows] fp32 is written with a stride of loss_stride floats.
+ * scale is the upstream factor (1/N for a mean over N tokens).
+ */
+flce_status flce_ce_rows(float* z, int64_t ldz, const int32_t* targets,
+                         int64_t rows, int64_t V, float scale,
+                         float* row_loss, int64_t loss_stride, flce_dtype dt,
+                         hipStream_t stream);
+
+/* A static, human-readable name for a status code (host only). */
+const char* flce_status_string(flce_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H_ */

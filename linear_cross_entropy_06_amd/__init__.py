@@ -1,0 +1,31 @@
+"""Fused linear + cross-entropy loss head for AMD Instinct MI355X (gfx950).
+
+The work is done by libflce.so (HIP kernels behind the C ABI in
+include/flce.h); this package is its Python binding.
+"""
+
+from ._lib import (
+    EXPORTS,
+    FLCE_BF16,
+    FLCE_F32,
+    FlceError,
+    LIB_PATH,
+    ce_rows,
+    fwd_bwd,
+    load,
+    logits,
+    workspace_bytes,
+)
+
+__all__ = [
+    "EXPORTS",
+    "FLCE_BF16",
+    "FLCE_F32",
+    "FlceError",
+    "LIB_PATH",
+    "ce_rows",
+    "fwd_bwd",
+    "load",
+    "logits",
+    "workspace_bytes",
+]

@@ -1,0 +1,177 @@
+"""ctypes binding of libflce.so (the C ABI declared in include/flce.h).
+
+Argument marshalling only: tensors are checked for device, dtype and
+layout, outputs are allocated with torch on the tensors' device, and raw
+device pointers plus the current HIP stream are handed to the library.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback.  If the library is not built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libflce.so")
+
+FLCE_BF16 = 0
+FLCE_F32 = 1
+
+STATUS = {
+    0: "FLCE_OK",
+    1: "FLCE_ERR_INVALID_ARG",
+    2: "FLCE_ERR_WORKSPACE",
+    3: "FLCE_ERR_UNSUPPORTED",
+    4: "FLCE_ERR_HIP",
+}
+
+# Every entry point include/flce.h declares.
+EXPORTS = (
+    "flce_workspace_bytes",
+    "flce_fwd_bwd",
+    "flce_logits",
+    "flce_ce_rows",
+    "flce_status_string",
+)
+
+_lib = None
+
+
+class FlceError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libflce.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m linear_cross_entropy_06_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    lib.flce_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.flce_workspace_bytes.restype = sz
+    lib.flce_fwd_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, sz,
+                                 ctypes.c_int, vp]
+    lib.flce_fwd_bwd.restype = ctypes.c_int
+    lib.flce_logits.argtypes = [vp, vp, i64, i64, i64, vp, i64, ctypes.c_int, vp]
+    lib.flce_logits.restype = ctypes.c_int
+    lib.flce_ce_rows.argtypes = [vp, i64, vp, i64, i64, ctypes.c_float, vp, i64,
+                                 ctypes.c_int, vp]
+    lib.flce_ce_rows.restype = ctypes.c_int
+    lib.flce_status_string.argtypes = [ctypes.c_int]
+    lib.flce_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load().flce_status_string(status).decode()
+        raise FlceError(status, msg)
+
+
+def _dt(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return FLCE_BF16
+    if x.dtype == torch.float32:
+        return FLCE_F32
+    raise TypeError(f"unsupported dtype {x.dtype}; expected bfloat16 or float32")
+
+
+def _stream_ptr(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need_cuda(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def workspace_bytes(N: int, H: int, V: int, chunk: int, dtype: torch.dtype) -> int:
+    dt = FLCE_BF16 if dtype == torch.bfloat16 else FLCE_F32
+    return int(load().flce_workspace_bytes(N, H, V, chunk, dt))
+
+
+def fwd_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+            chunk: Optional[int] = None, *,
+            loss: Optional[torch.Tensor] = None,
+            grad_h: Optional[torch.Tensor] = None,
+            grad_W: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None,
+            ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Mean cross-entropy loss of h W^T against targets, with dloss/dh and
+    dloss/dW, via ``flce_fwd_bwd``.  Returns (loss [] fp32, grad_h like h,
+    grad_W [V, H] fp32).  Buffers may be passed in to avoid allocation."""
+    lib = load()
+    _need_cuda(h, W, targets)
+    if targets.dtype != torch.int32:
+        raise TypeError("targets must be int32")
+    if W.dtype != h.dtype:
+        raise TypeError("h and W must share a dtype")
+    N, H = h.shape
+    V = W.shape[0]
+    chunk = N if chunk is None else int(chunk)
+    dt = _dt(h)
+    dev = h.device
+    if loss is None:
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+    if grad_h is None:
+        grad_h = torch.empty_like(h)
+    if grad_W is None:
+        grad_W = torch.empty((V, H), dtype=torch.float32, device=dev)
+    need = int(lib.flce_workspace_bytes(N, H, V, chunk, dt))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need_cuda(loss, grad_h, grad_W, workspace)
+    st = lib.flce_fwd_bwd(h.data_ptr(), W.data_ptr(), targets.data_ptr(), N, H, V, chunk,
+                          loss.data_ptr(), grad_h.data_ptr(), grad_W.data_ptr(),
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          dt, _stream_ptr(dev))
+    _check(st)
+    return loss, grad_h, grad_W
+
+
+def logits(h: torch.Tensor, W: torch.Tensor, z: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 logits h W^T via ``flce_logits`` (the first step alone)."""
+    lib = load()
+    _need_cuda(h, W)
+    rows, H = h.shape
+    V = W.shape[0]
+    if z is None:
+        z = torch.empty((rows, V), dtype=torch.float32, device=h.device)
+    _need_cuda(z)
+    _check(lib.flce_logits(h.data_ptr(), W.data_ptr(), rows, H, V, z.data_ptr(), z.stride(0),
+                           _dt(h), _stream_ptr(h.device)))
+    return z
+
+
+def ce_rows(z: torch.Tensor, targets: torch.Tensor, scale: float, out_dtype: torch.dtype,
+            row_loss: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Row losses of fp32 logits z, rewriting z in place with the scaled
+    logit gradient (``flce_ce_rows``).  For bf16 the gradient of row i is
+    z.view(int16)[i, :V] viewed with a pitch of 2 * z.stride(0)."""
+    lib = load()
+    _need_cuda(z, targets)
+    if z.dtype != torch.float32 or targets.dtype != torch.int32:
+        raise TypeError("z must be float32 and targets int32")
+    rows, V = z.shape
+    if row_loss is None:
+        row_loss = torch.empty(rows, dtype=torch.float32, device=z.device)
+    dt = FLCE_BF16 if out_dtype == torch.bfloat16 else FLCE_F32
+    _check(lib.flce_ce_rows(z.data_ptr(), z.stride(0), targets.data_ptr(), rows, V,
+                            float(scale), row_loss.data_ptr(), 1, dt,
+                            _stream_ptr(z.device)))
+    return row_loss

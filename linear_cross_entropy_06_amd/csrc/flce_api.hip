@@ -1,0 +1,154 @@
+// C ABI of the fused linear + cross-entropy head: argument checks, the token
+// chunk loop and the kernel launches.  Host code only; nothing here
+// allocates, synchronises or reads device memory.
+//
+// Per token chunk of C rows (page 1, "Liger Kernel explained", section
+// "What does Liger Kernel actually fuse": only a chunk of logits is ever
+// resident, and its gradient is formed before the next chunk):
+//   1. logits   Z[C, V] (fp32, workspace)  = h_c W^T          MFMA
+//   2. rows     lse, row loss -> staged in grad_h's rows of the chunk;
+//               Z rewritten in place as G = (softmax - onehot) / N
+//   3. loss     *loss (+)= sum(staged row losses) / N         fixed order
+//   4. grad_h   grad_h_c = G W      (overwrites the staged losses)
+//   5. grad_W   grad_W (+)= G^T h_c (written by the first chunk, then
+//               accumulated in fp32)
+#include "flce.h"
+#include "flce_internal.h"
+
+#include <stdint.h>
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool dims_ok(int64_t a) { return a >= 1 && a <= kMaxDim; }
+
+inline bool dtype_ok(flce_dtype dt) { return dt == FLCE_BF16 || dt == FLCE_F32; }
+
+inline int64_t esize(flce_dtype dt) { return dt == FLCE_BF16 ? 2 : 4; }
+
+inline hipError_t gemm(flce_dtype dt, bool a_kc, bool b_kc, int epi, bool vec,
+                       const flce::GemmArgs& g, hipStream_t s) {
+  return dt == FLCE_BF16 ? flce::launch_gemm_bf16(a_kc, b_kc, epi, vec, g, s)
+                         : flce::launch_gemm_f32(a_kc, b_kc, epi, g, s);
+}
+
+}  // namespace
+
+extern "C" size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk,
+                                       flce_dtype dt) {
+  if (!dims_ok(N) || !dims_ok(H) || !dims_ok(V) || chunk < 1 || !dtype_ok(dt)) return 0;
+  const int64_t C = chunk < N ? chunk : N;
+  return static_cast<size_t>(C) * static_cast<size_t>(V) * 4u;
+}
+
+extern "C" flce_status flce_fwd_bwd(const void* h, const void* W, const int32_t* targets,
+                                    int64_t N, int64_t H, int64_t V, int64_t chunk,
+                                    float* loss, void* grad_h, float* grad_W,
+                                    void* workspace, size_t workspace_bytes, flce_dtype dt,
+                                    hipStream_t stream) {
+  if (!h || !W || !targets || !loss || !grad_h || !grad_W || !workspace)
+    return FLCE_ERR_INVALID_ARG;
+  if (!dims_ok(N) || !dims_ok(H) || !dims_ok(V) || chunk < 1 || !dtype_ok(dt))
+    return FLCE_ERR_INVALID_ARG;
+  if (H % 8 != 0) return FLCE_ERR_UNSUPPORTED;
+  if (!aligned16(h) || !aligned16(W) || !aligned16(grad_h) || !aligned16(grad_W) ||
+      !aligned16(workspace) || (reinterpret_cast<uintptr_t>(targets) & 3u) ||
+      (reinterpret_cast<uintptr_t>(loss) & 3u))
+    return FLCE_ERR_UNSUPPORTED;
+  const size_t need = flce_workspace_bytes(N, H, V, chunk, dt);
+  if (workspace_bytes < need) return FLCE_ERR_WORKSPACE;
+
+  const int64_t C = chunk < N ? chunk : N;
+  const int64_t es = esize(dt);
+  const bool bf16 = dt == FLCE_BF16;
+  const bool vec = (V % 8) == 0;
+  const float inv_n = static_cast<float>(1.0 / static_cast<double>(N));
+  // G's row pitch in its own elements: bf16 G lives in the first half of
+  // each fp32 logit row, fp32 G replaces the row.
+  const int64_t ldg = bf16 ? 2 * V : V;
+  float* z = static_cast<float*>(workspace);
+  const int64_t loss_stride = H * es / 4;  // floats between staged row losses
+
+  for (int64_t r0 = 0; r0 < N; r0 += C) {
+    const int rows = static_cast<int>((N - r0) < C ? (N - r0) : C);
+    const char* hc = static_cast<const char*>(h) + r0 * H * es;
+    char* ghc = static_cast<char*>(grad_h) + r0 * H * es;
+    float* staged = reinterpret_cast<float*>(ghc);
+    hipError_t e;
+
+    // 1. Z^T = W . h_c^T, stored as Z[i][j] (row pitch V floats).
+    flce::GemmArgs g1{W, H, hc, H, z, V, static_cast<int>(V), rows, static_cast<int>(H), 0};
+    if ((e = gemm(dt, true, true, flce::kStoreF32, vec, g1, stream)) != hipSuccess)
+      return FLCE_ERR_HIP;
+
+    // 2. lse and row losses; Z -> G in place.
+    if ((e = flce::launch_ce_rows(z, V, targets + r0, rows, static_cast<int>(V), inv_n,
+                                  staged, loss_stride, bf16, stream)) != hipSuccess)
+      return FLCE_ERR_HIP;
+
+    // 3. running mean loss.
+    if ((e = flce::launch_loss_sum(staged, loss_stride, rows, inv_n, r0 == 0 ? 1 : 0, loss,
+                                   stream)) != hipSuccess)
+      return FLCE_ERR_HIP;
+
+    // 4. grad_h_c^T = W^T . G^T: A(m = hidden, k = vocab) = W[k][m],
+    //    B(n = token, k = vocab) = G[n][k].
+    flce::GemmArgs g4{W, H, z, ldg, ghc, H, static_cast<int>(H), rows, static_cast<int>(V), 0};
+    if ((e = gemm(dt, false, true, flce::kStoreOut, vec, g4, stream)) != hipSuccess)
+      return FLCE_ERR_HIP;
+
+    // 5. grad_W^T (+)= h_c^T . G: A(m = hidden, k = token) = h_c[k][m],
+    //    B(n = vocab, k = token) = G[k][n].
+    flce::GemmArgs g5{hc, H, z, ldg, grad_W, H, static_cast<int>(H), static_cast<int>(V), rows,
+                      r0 == 0 ? 0 : 1};
+    if ((e = gemm(dt, false, false, flce::kAccumF32, vec, g5, stream)) != hipSuccess)
+      return FLCE_ERR_HIP;
+  }
+  return FLCE_OK;
+}
+
+extern "C" flce_status flce_logits(const void* h, const void* W, int64_t rows, int64_t H,
+                                   int64_t V, float* z, int64_t ldz, flce_dtype dt,
+                                   hipStream_t stream) {
+  if (!h || !W || !z) return FLCE_ERR_INVALID_ARG;
+  if (!dims_ok(rows) || !dims_ok(H) || !dims_ok(V) || ldz < V || !dtype_ok(dt))
+    return FLCE_ERR_INVALID_ARG;
+  if (H % 8 != 0) return FLCE_ERR_UNSUPPORTED;
+  if (!aligned16(h) || !aligned16(W) || !aligned16(z)) return FLCE_ERR_UNSUPPORTED;
+  const bool vec = (ldz % 4) == 0;
+  flce::GemmArgs g{W, H, h, H, z, ldz, static_cast<int>(V), static_cast<int>(rows),
+                   static_cast<int>(H), 0};
+  return gemm(dt, true, true, flce::kStoreF32, vec, g, stream) == hipSuccess ? FLCE_OK
+                                                                             : FLCE_ERR_HIP;
+}
+
+extern "C" flce_status flce_ce_rows(float* z, int64_t ldz, const int32_t* targets,
+                                    int64_t rows, int64_t V, float scale, float* row_loss,
+                                    int64_t loss_stride, flce_dtype dt, hipStream_t stream) {
+  if (!z || !targets || !row_loss) return FLCE_ERR_INVALID_ARG;
+  if (!dims_ok(rows) || !dims_ok(V) || ldz < V || loss_stride < 1 || !dtype_ok(dt))
+    return FLCE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(z) & 3u) || (reinterpret_cast<uintptr_t>(targets) & 3u) ||
+      (reinterpret_cast<uintptr_t>(row_loss) & 3u))
+    return FLCE_ERR_UNSUPPORTED;
+  return flce::launch_ce_rows(z, ldz, targets, static_cast<int>(rows), static_cast<int>(V),
+                              scale, row_loss, loss_stride, dt == FLCE_BF16, stream) ==
+                 hipSuccess
+             ? FLCE_OK
+             : FLCE_ERR_HIP;
+}
+
+extern "C" const char* flce_status_string(flce_status s) {
+  switch (s) {
+    case FLCE_OK: return "FLCE_OK";
+    case FLCE_ERR_INVALID_ARG: return "FLCE_ERR_INVALID_ARG: null pointer, bad size or dtype";
+    case FLCE_ERR_WORKSPACE: return "FLCE_ERR_WORKSPACE: workspace smaller than required";
+    case FLCE_ERR_UNSUPPORTED:
+      return "FLCE_ERR_UNSUPPORTED: H % 8 != 0 or a pointer is not 16-byte aligned";
+    case FLCE_ERR_HIP: return "FLCE_ERR_HIP: the HIP runtime reported a launch error";
+  }
+  return "unknown flce_status";
+}

@@ -1,0 +1,70 @@
+"""Write the oracle's expected values for the full-size workloads.
+
+    python tests/golden/make_golden.py [config ...]      (default: 2 3 4 5)
+
+Calls only ``synth`` (seeded inputs) and ``oracle`` (fp64 reference).  For
+each workload it stores, in ``cfg<k>_sampled.npz``: the mean loss, the
+per-row log-sum-exp of every token, a set of sampled token rows with their
+grad_h rows and a set of sampled vocabulary rows with their grad_W rows
+(gradients stored as float32).
+"""
+
+from __future__ import annotations
+
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from synth import CONFIGS, make_inputs, to_float64  # noqa: E402
+
+
+def sample_rows(cfg, t: np.ndarray):
+    """Token rows at both ends, at chunk edges of the benchmark's chunk and
+    a few seeded random ones; vocabulary rows at both ends, the most
+    frequent target, targets of sampled tokens and a few random ones."""
+    N, V = cfg.N, cfg.V
+    C = cfg.default_chunk
+    rng = np.random.default_rng([0, 99])
+    rows = {0, 1, N // 2, N - 2, N - 1, C - 1, min(C, N - 1), 2047 % N, 2048 % N}
+    rows |= set(rng.integers(0, N, 4).tolist())
+    vals, counts = np.unique(t, return_counts=True)
+    vocab = {0, 1, V // 2, V - 1, int(vals[np.argmax(counts)]), int(t[0]), int(t[N - 1])}
+    vocab |= set(rng.integers(0, V, 4).tolist())
+    return np.array(sorted(rows)), np.array(sorted(vocab))
+
+
+def make(idx: int) -> str:
+    cfg = CONFIGS[idx]
+    t0 = time.perf_counter()
+    x = make_inputs(cfg, seed=0)
+    h, W, t = to_float64(x.h), to_float64(x.W), x.t.numpy().astype(np.int64)
+    rows, vocab = sample_rows(cfg, t)
+    r = oracle.flce_sampled(h, W, t, rows=rows, vocab_rows=vocab, chunk=1024)
+    out = os.path.join(HERE, f"cfg{idx}_sampled.npz")
+    np.savez_compressed(
+        out,
+        config=np.array(cfg.name),
+        seed=np.array(0),
+        loss=np.array(r["loss"]),
+        lse=r["lse"].astype(np.float64),
+        rows=rows,
+        vocab_rows=vocab,
+        grad_h_rows=r["grad_h_rows"].astype(np.float32),
+        grad_W_rows=r["grad_W_rows"].astype(np.float32),
+    )
+    print(f"cfg{idx} {cfg.name}: loss={r['loss']:.9f} rows={len(rows)} "
+          f"vocab_rows={len(vocab)} ({time.perf_counter() - t0:.1f} s) -> {out}", flush=True)
+    return out
+
+
+if __name__ == "__main__":
+    ids = [int(a) for a in sys.argv[1:]] or [2, 3, 4, 5]
+    for i in ids:
+        make(i)

@@ -1,0 +1,321 @@
+"""GPU parity of the HIP path (libflce.so via its C ABI) with the fp64 oracle.
+
+Every case feeds the same stored input values (bf16 or fp32 bits from
+``synth``) to the GPU and, upcast exactly to fp64, to ``oracle``.  Small
+cases are compared element by element; full-size workloads are compared on
+sampled rows against values the oracle wrote to tests/golden/ (see
+make_golden.py), plus properties that hold at any size.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, make_inputs, make_random, to_float64
+from parity_util import (GRAD_RTOL, LOSS_RTOL, bf16_rows_from_workspace, f64, rel,
+                         rel_fro, say, to_device)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def flce():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_cross_entropy_06_amd as m
+    m.load()  # raises if the HIP library is missing: no fallback exists
+    return m
+
+
+def _oracle(inp):
+    h, W, t = to_float64(inp.h), to_float64(inp.W), inp.t.numpy().astype(np.int64)
+    return oracle.flce(h, W, t)
+
+
+def _check_full(name, got, exp, loss_rtol=LOSS_RTOL, grad_rtol=GRAD_RTOL):
+    loss, gh, gw = got
+    l0, gh0, gw0 = exp
+    el, eh, ew = rel(float(loss), l0), rel_fro(f64(gh), gh0), rel_fro(f64(gw), gw0)
+    say(f"{name}: loss {float(loss):.7f} vs {l0:.7f} rel {el:.2e}; "
+        f"grad_h rel_fro {eh:.2e}; grad_W rel_fro {ew:.2e}")
+    assert np.isfinite(float(loss))
+    assert el <= loss_rtol, (name, el)
+    assert eh <= grad_rtol, (name, eh)
+    assert ew <= grad_rtol, (name, ew)
+    return el, eh, ew
+
+
+# ---------------------------------------------------------------------------
+# step 1 alone: the MFMA logits GEMM
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,H,V", [(37, 72, 300), (300, 200, 600), (256, 128, 1000),
+                                   (5, 8, 517), (513, 264, 64)])
+def test_logits_gemm(flce, N, H, V):
+    inp = make_random(N, H, V, dtype="bf16", seed=N + V, w_std=0.5)
+    h, W, _ = to_device(inp)
+    say(f"flce_logits N={N} H={H} V={V}")
+    z = flce.logits(h, W)
+    torch.cuda.synchronize()
+    ref = oracle.logits(to_float64(inp.h), to_float64(inp.W))
+    err = np.abs(f64(z) - ref).max() / np.abs(ref).max()
+    say(f"  max rel err {err:.2e}")
+    assert err < 2e-6
+
+
+def test_logits_gemm_fp32(flce):
+    inp = make_random(70, 40, 130, dtype="f32", seed=3, w_std=0.5)
+    h, W, _ = to_device(inp)
+    say("flce_logits fp32 70x40x130")
+    z = flce.logits(h, W)
+    torch.cuda.synchronize()
+    ref = oracle.logits(to_float64(inp.h), to_float64(inp.W))
+    assert np.abs(f64(z) - ref).max() / np.abs(ref).max() < 2e-6
+
+
+# ---------------------------------------------------------------------------
+# steps 2-3 alone: per-row cross entropy and the in-place gradient rewrite
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,V,std", [(37, 1000, 3.0), (9, 5, 1.0), (4, 1, 1.0),
+                                        (64, 4099, 8.0), (3, 128256, 1.0)])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_ce_rows(flce, rows, V, std, out):
+    g = torch.Generator().manual_seed(rows * 7 + V)
+    z_cpu = torch.randn(rows, V, generator=g, dtype=torch.float32) * std
+    t_cpu = torch.randint(0, V, (rows,), generator=g, dtype=torch.int32)
+    Z = f64(z_cpu)
+    tt = t_cpu.numpy().astype(np.int64)
+    scale = 1.0 / 1000.0
+    exp_loss = oracle.row_losses(Z, tt)
+    exp_G = oracle.dlogits(Z, tt, 1) * scale
+    z = z_cpu.cuda()
+    say(f"flce_ce_rows rows={rows} V={V} out={out}")
+    rl = flce.ce_rows(z, t_cpu.cuda(), scale, torch.bfloat16 if out == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    got_loss = f64(rl)
+    assert np.abs(got_loss - exp_loss).max() <= 1e-5 * max(1.0, np.abs(exp_loss).max())
+    G = bf16_rows_from_workspace(z, rows, V) if out == "bf16" else f64(z)
+    e = rel_fro(G, exp_G) if np.linalg.norm(exp_G) > 0 else np.abs(G).max()
+    say(f"  G rel_fro {e:.2e}")
+    assert e <= (4e-3 if out == "bf16" else 1e-5)
+    # each row of (softmax - onehot) sums to zero
+    assert np.abs(G.sum(axis=1)).max() <= 1e-2 * scale + 1e-12
+
+
+# ---------------------------------------------------------------------------
+# the whole call on small shapes: ragged chunks and tails, tiny vocabularies
+# ---------------------------------------------------------------------------
+
+TINY = [
+    # N, H, V, chunk, dtype
+    (1, 8, 1, 1, "bf16"),
+    (3, 8, 5, 1, "bf16"),
+    (3, 24, 5, 3, "bf16"),
+    (17, 24, 1000, 7, "bf16"),
+    (17, 8, 1000, 17, "bf16"),
+    (17, 24, 5, 7, "bf16"),
+    (300, 136, 520, 100, "bf16"),
+    (300, 136, 523, 256, "bf16"),
+    (513, 264, 1000, 257, "bf16"),
+    (3, 8, 5, 2, "f32"),
+    (17, 24, 1000, 7, "f32"),
+    (100, 64, 333, 33, "f32"),
+]
+
+
+@pytest.mark.parametrize("N,H,V,chunk,dtype", TINY)
+def test_fwd_bwd_small(flce, N, H, V, chunk, dtype):
+    inp = make_random(N, H, V, dtype=dtype, seed=N * 31 + V, w_std=0.3)
+    h, W, t = to_device(inp)
+    say(f"flce_fwd_bwd N={N} H={H} V={V} chunk={chunk} {dtype}")
+    got = flce.fwd_bwd(h, W, t, chunk)
+    torch.cuda.synchronize()
+    exp = _oracle(inp)
+    if V == 1:
+        # one class: loss 0, gradients 0
+        assert abs(float(got[0])) < 1e-6
+        assert f64(got[1]).max() == 0 and np.abs(f64(got[2])).max() == 0
+        return
+    _check_full(f"small{(N, H, V, chunk, dtype)}", got, exp)
+
+
+def test_config1_fp32(flce):
+    """The tiny fp32 workload at the chunk sizes 256, 64 and 100."""
+    cfg = CONFIGS[1]
+    inp = make_inputs(cfg, seed=0)
+    exp = _oracle(inp)
+    h, W, t = to_device(inp)
+    for c in (256, 64, 100):
+        say(f"config 1 chunk={c}")
+        got = flce.fwd_bwd(h, W, t, c)
+        torch.cuda.synchronize()
+        el, eh, ew = _check_full(f"cfg1/c{c}", got, exp)
+        # fp32 operands and an fp32 logit gradient: far inside the bar
+        assert el < 1e-5 and eh < 1e-4 and ew < 1e-4
+
+
+def test_config2_full(flce):
+    """Llama-2-7B-like head (N=2048, H=4096, V=32000): every element."""
+    cfg = CONFIGS[2]
+    inp = make_inputs(cfg, seed=0)
+    h, W, t = to_device(inp)
+    say("config 2 full, chunk 2048")
+    got = flce.fwd_bwd(h, W, t, 2048)
+    torch.cuda.synchronize()
+    got = tuple(x.cpu() for x in got)
+    h64, W64 = to_float64(inp.h), to_float64(inp.W)
+    exp = oracle.flce_chunked(h64, W64, inp.t.numpy().astype(np.int64), 512)
+    _check_full("cfg2", got, exp)
+    say("config 2 chunk 512 vs chunk 2048")
+    got2 = flce.fwd_bwd(h, W, t, 512)
+    torch.cuda.synchronize()
+    _check_full("cfg2/c512", tuple(x.cpu() for x in got2), exp)
+
+
+def _golden(idx):
+    p = os.path.join(GOLDEN, f"cfg{idx}_sampled.npz")
+    if not os.path.exists(p):
+        pytest.fail(f"missing {p}: run tests/golden/make_golden.py {idx}")
+    return np.load(p, allow_pickle=False)
+
+
+@pytest.mark.parametrize("idx", [3, 4, 5])
+def test_full_size_sampled(flce, idx):
+    """Full-size workloads at the benchmark's chunk: loss and sampled rows
+    against the oracle's stored values, plus sum_j grad_W[j, :] = 0."""
+    cfg = CONFIGS[idx]
+    gold = _golden(idx)
+    say(f"config {idx} ({cfg.name}): generating inputs")
+    inp = make_inputs(cfg, seed=0)
+    h, W, t = to_device(inp)
+    del inp
+    C = cfg.default_chunk
+    say(f"config {idx} fwd_bwd chunk={C}")
+    loss, gh, gw = flce.fwd_bwd(h, W, t, C)
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(gold["rows"]).cuda()
+    vrows = torch.from_numpy(gold["vocab_rows"]).cuda()
+    el = rel(float(loss), float(gold["loss"]))
+    eh = rel_fro(f64(gh[rows]), gold["grad_h_rows"])
+    ew = rel_fro(f64(gw[vrows]), gold["grad_W_rows"])
+    colsum = gw.double().sum(dim=0).abs().max().item()
+    scale = gw.double().abs().sum(dim=0).max().item()
+    say(f"  loss {float(loss):.6f} vs {float(gold['loss']):.6f} rel {el:.2e}; "
+        f"grad_h rows rel_fro {eh:.2e}; grad_W rows rel_fro {ew:.2e}; "
+        f"|sum_j grad_W| {colsum:.2e} (sum |.| {scale:.2e})")
+    assert el <= LOSS_RTOL
+    assert eh <= GRAD_RTOL
+    assert ew <= GRAD_RTOL
+    assert colsum <= 1e-3 * scale
+
+
+# ---------------------------------------------------------------------------
+# closed forms, invariants, determinism, memory
+# ---------------------------------------------------------------------------
+
+def test_closed_forms_on_gpu(flce):
+    N, H, V = 300, 64, 1000
+    inp = make_random(N, H, V, dtype="bf16", seed=5)
+    h, W, t = to_device(inp)
+    say("W = 0 closed form")
+    loss, gh, gw = flce.fwd_bwd(h, torch.zeros_like(W), t, 128)
+    torch.cuda.synchronize()
+    assert rel(float(loss), math.log(V)) < 1e-6
+    assert torch.count_nonzero(gh).item() == 0          # exactly zero
+    hh = to_float64(inp.h)
+    exp_gw = np.tile(hh.sum(axis=0) / V, (V, 1))
+    np.add.at(exp_gw, inp.t.numpy(), -hh)
+    assert rel_fro(f64(gw), exp_gw / N) < GRAD_RTOL
+    say("h = 0 closed form")
+    loss, gh, gw = flce.fwd_bwd(torch.zeros_like(h), W, t, 128)
+    torch.cuda.synchronize()
+    assert rel(float(loss), math.log(V)) < 1e-6
+    assert torch.count_nonzero(gw).item() == 0
+    WW = to_float64(inp.W)
+    exp_gh = (WW.mean(axis=0)[None, :] - WW[inp.t.numpy()]) / N
+    assert rel_fro(f64(gh), exp_gh) < GRAD_RTOL
+
+
+def test_chunk_invariance_and_determinism(flce):
+    N, H, V = 1000, 256, 3000
+    inp = make_random(N, H, V, dtype="bf16", seed=6, w_std=0.1)
+    h, W, t = to_device(inp)
+    exp = _oracle(inp)
+    outs = {}
+    for c in (N, 250, 333, 1):
+        say(f"chunk invariance chunk={c}")
+        outs[c] = tuple(x.clone() for x in flce.fwd_bwd(h, W, t, c))
+        torch.cuda.synchronize()
+        _check_full(f"chunk{c}", outs[c], exp)
+    # same chunk, same bits
+    say("determinism")
+    again = flce.fwd_bwd(h, W, t, 333)
+    torch.cuda.synchronize()
+    for a, b in zip(outs[333], again):
+        assert torch.equal(a, b)
+    # different chunks agree to rounding
+    assert rel(float(outs[250][0]), float(outs[N][0])) < 1e-5
+    assert rel_fro(f64(outs[250][2]), f64(outs[N][2])) < 2e-3
+
+
+def test_no_hidden_allocation(flce):
+    cfg = CONFIGS[2]
+    N, H, V = 2048, 1024, 32000
+    inp = make_random(N, H, V, dtype="bf16", seed=8)
+    h, W, t = to_device(inp)
+    C = 512
+    loss = torch.empty((), dtype=torch.float32, device="cuda")
+    gh = torch.empty_like(h)
+    gw = torch.empty((V, H), dtype=torch.float32, device="cuda")
+    need = flce.workspace_bytes(N, H, V, C, torch.bfloat16)
+    assert need == C * V * 4 < cfg.naive_logits_bytes
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.max_memory_allocated()
+    say("no hidden allocation")
+    flce.fwd_bwd(h, W, t, C, loss=loss, grad_h=gh, grad_W=gw, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() == base
+    with pytest.raises(flce.FlceError):
+        flce.fwd_bwd(h, W, t, C, loss=loss, grad_h=gh, grad_W=gw, workspace=ws[: need - 16])
+
+
+def test_large_logits_stress(flce):
+    """Page 3's own example draws h and W from N(0, 1) (logit spread ~64):
+    the max-shifted reduction must stay finite and accurate."""
+    N, H, V = 256, 4096, 128256
+    inp = make_random(N, H, V, dtype="bf16", seed=9, h_std=1.0, w_std=1.0)
+    h, W, t = to_device(inp)
+    say("stress N(0,1) weights, N=256 H=4096 V=128256")
+    loss, gh, gw = flce.fwd_bwd(h, W, t, 128)
+    torch.cuda.synchronize()
+    assert math.isfinite(float(loss))
+    assert torch.isfinite(gh.float()).all() and torch.isfinite(gw).all()
+    hh, WW = to_float64(inp.h), to_float64(inp.W)
+    tt = inp.t.numpy().astype(np.int64)
+    rows = np.array([0, 1, 127, 128, 255])
+    vrows = np.unique(np.concatenate([tt[:4], [0, V - 1]]))
+    r = oracle.flce_sampled(hh, WW, tt, rows=rows, vocab_rows=vrows, chunk=128)
+    el = rel(float(loss), r["loss"])
+    eh = rel_fro(f64(gh)[rows], r["grad_h_rows"])
+    ew = rel_fro(f64(gw)[vrows], r["grad_W_rows"])
+    say(f"  loss rel {el:.2e} grad_h rel_fro {eh:.2e} grad_W rel_fro {ew:.2e}")
+    assert el <= LOSS_RTOL and eh <= GRAD_RTOL and ew <= GRAD_RTOL
+
+
+def test_out_of_range_target_is_nan_not_a_fault(flce):
+    inp = make_random(8, 16, 50, dtype="bf16", seed=10)
+    h, W, t = to_device(inp)
+    t[3] = 50
+    say("out-of-range target")
+    loss, gh, gw = flce.fwd_bwd(h, W, t, 8)
+    torch.cuda.synchronize()
+    assert math.isnan(float(loss))
