@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Throughput of the fused linear + cross-entropy head (forward + backward).
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 3] [--workload llama3_8b_head]
+                    [--chunk C] [--no-cpu-baseline] [--cpu-sample-tokens S]
+
+One step = one flce_fwd_bwd call over the whole batch of the workload
+(every token chunk: logits GEMM, row log-sum-exp + gradient rewrite, loss
+sum, grad_h GEMM, grad_W GEMM), with inputs already resident in HBM.  The
+timed region is bracketed by torch.cuda.synchronize() on both sides.  Prints
+one JSON line.
+
+roofline: the dominant kernel (the step with the largest share of GPU time)
+timed live with HIP events recorded by flce_fwd_bwd_timed around every
+launch, on the stream the kernels run on; achieved = its algorithmic work
+per launch (2 * M * N * K flops of one chunk's contraction) / its mean
+launch duration.
+cpu_baseline: the fp64 CPU oracle on the first S tokens of the same
+workload (full V x H head), timed on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FLCE fwd+bwd tokens/s + % bf16 MFMA peak; peak workspace bytes"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "llama3_8b_head"
+GEMM_STEPS = ("logits_gemm", "grad_h_gemm", "grad_W_gemm")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3_8b_head.md")
+KERNEL_SOURCES = ("gemm_bf16.hip", "ce_rows.hip", "flce_api.hip", "flce_internal.h")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--chunk", type=int, default=0, help="token chunk (default: workload's)")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    return p.parse_args()
+
+
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "linear_cross_entropy_06_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(step: str, workload: str):
+    """HBM bytes per launch of `step` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"sources_digest:\s*([0-9a-f]+)", text)
+    if not m or m.group(1) != sources_digest():
+        return None
+    m = re.search(rf"traffic_bytes_per_launch\[{re.escape(workload)}/{re.escape(step)}\]:"
+                  rf"\s*([0-9.eE+]+)", text)
+    return float(m.group(1)) if m else None
+
+
+def cpu_baseline(inp, cfg, sample_tokens: int, chunk: int):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from synth import to_float64
+
+    S = min(sample_tokens, cfg.N)
+    cores = len(os.sched_getaffinity(0))
+    blas_threads = max([d.get("num_threads", 0) for d in threadpool_info()] or [cores])
+    h64 = to_float64(inp.h[:S])
+    W64 = to_float64(inp.W)
+    t = inp.t[:S].numpy().astype(np.int64)
+    t0 = time.perf_counter()
+    loss, _, _ = oracle.flce_chunked(h64, W64, t, chunk)
+    dt = time.perf_counter() - t0
+    return {
+        "value": S / dt,
+        "unit": "tokens/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"first {S} of {cfg.N} tokens of {cfg.name} against the full "
+                   f"{cfg.V}x{cfg.H} head, fp64 numpy oracle, token chunk {chunk}: "
+                   f"{dt:.2f} s for {6.0 * S * cfg.V * cfg.H / 1e12:.2f} TFLOP "
+                   f"({cores} cores available)"),
+    }
+
+
+def main() -> int:
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the head shards over tokens with one grad_W "
+              "all-reduce, which is not part of this build", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import linear_cross_entropy_06_amd as flce
+    from synth import config_by_name, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    flce.load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg = config_by_name(args.workload)
+    N, H, V = cfg.N, cfg.H, cfg.V
+    C = args.chunk or cfg.default_chunk or N
+    dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    t_gen = time.perf_counter()
+    inp = make_inputs(cfg, seed=args.seed)
+    h, W, t = inp.h.to(dev), inp.W.to(dev), inp.t.to(dev)
+    t_gen = time.perf_counter() - t_gen
+
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    gh = torch.empty_like(h)
+    gw = torch.empty((V, H), dtype=torch.float32, device=dev)
+    ws_bytes = flce.workspace_bytes(N, H, V, C, dtype)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    L = flce.launch_count(N, C)
+    events = [flce.HipEvents(2 * L) for _ in range(args.steps)]
+
+    for _ in range(args.warmup):
+        flce.fwd_bwd(h, W, t, C, loss=loss, grad_h=gh, grad_W=gw, workspace=ws)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    mem_before = torch.cuda.max_memory_allocated()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        flce.fwd_bwd(h, W, t, C, loss=loss, grad_h=gh, grad_W=gw, workspace=ws,
+                     events=events[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    hidden_alloc = torch.cuda.max_memory_allocated() - mem_before
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tok_s = N / (ms_per_step * 1e-3)
+    flops = 6.0 * N * V * H
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+
+    # per-step kernel durations from the events
+    per_step = {name: [] for name in flce.STEP_NAMES}
+    for ev in events:
+        for l in range(L):
+            per_step[flce.STEP_NAMES[l % flce.FLCE_STEPS]].append(ev.elapsed_ms(2 * l, 2 * l + 1))
+    gpu_ms = [ev.elapsed_ms(0, 2 * L - 1) for ev in events]
+    for ev in events:
+        ev.close()
+    avg_ms = {k: float(np.mean(v)) for k, v in per_step.items()}
+    tot_ms = {k: float(np.sum(v)) / args.steps for k, v in per_step.items()}
+    dominant = max(GEMM_STEPS, key=lambda k: tot_ms[k])
+    rows = C  # every chunk is full for the benchmark workloads when C divides N
+    flop_per_launch = 2.0 * rows * V * H
+    achieved = flop_per_launch / (avg_ms[dominant] * 1e-3) / 1e12
+    traffic = read_traffic(dominant, cfg.name)
+
+    loss_val = float(loss)
+    gold = os.path.join(ROOT, "tests", "golden", f"cfg{cfg.idx}_sampled.npz")
+    loss_ref = float(np.load(gold)["loss"]) if os.path.exists(gold) and args.seed == 0 else None
+
+    out = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": cfg.name, "N": N, "H": H, "V": V, "chunk": C,
+                   "seed": args.seed},
+        "tflops": tflops,
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "workspace_bytes": ws_bytes,
+        "naive_logits_bytes": cfg.naive_logits_bytes,
+        "workspace_frac_of_naive": ws_bytes / cfg.naive_logits_bytes,
+        "hidden_alloc_bytes": int(hidden_alloc),
+        "gpu_ms_per_step_events": float(np.median(gpu_ms)),
+        "kernel_ms_per_launch": avg_ms,
+        "kernel_share": {k: v / sum(tot_ms.values()) for k, v in tot_ms.items()},
+        "loss": loss_val,
+        "loss_rel_err_vs_oracle": (abs(loss_val - loss_ref) / abs(loss_ref)
+                                   if loss_ref else None),
+        "roofline": {
+            "kernel": dominant,
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "work_per_launch": f"2*{rows}*{V}*{H} = {flop_per_launch:.4e} flop",
+        },
+        "input_gen_s": t_gen,
+    }
+    if not args.no_cpu_baseline:
+        del h, W, t, gh, gw, ws
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_sample_tokens, 256)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -92,6 +92,31 @@ flce_status flce_fwd_bwd(const void* h, const void* W, const int32_t* targets,
                          flce_dtype dt, hipStream_t stream);
 
 /*
+ * Kernel launches flce_fwd_bwd makes for these sizes: FLCE_STEPS per token
+ * chunk, i.e. FLCE_STEPS * ceil(N / min(chunk, N)).  0 if a size is < 1.
+ */
+#define FLCE_STEPS 5
+int64_t flce_launch_count(int64_t N, int64_t chunk);
+
+/*
+ * flce_fwd_bwd that also records, on `stream`, events[2k] just before and
+ * events[2k + 1] just after its k-th kernel launch, so a caller can time
+ * each step with hipEventElapsedTime.  Launch k belongs to token chunk
+ * k / FLCE_STEPS and is step k % FLCE_STEPS of that chunk: 0 logits GEMM,
+ * 1 row log-sum-exp + gradient rewrite, 2 loss sum, 3 grad_h GEMM,
+ * 4 grad_W GEMM.  `events` is a HOST array of n_events handles the caller
+ * created (hipEventCreate) and owns; n_events must be at least
+ * 2 * flce_launch_count(N, chunk) (FLCE_ERR_INVALID_ARG otherwise).  The
+ * computation and every other rule are those of flce_fwd_bwd.
+ */
+flce_status flce_fwd_bwd_timed(const void* h, const void* W, const int32_t* targets,
+                               int64_t N, int64_t H, int64_t V, int64_t chunk,
+                               float* loss, void* grad_h, float* grad_W,
+                               void* workspace, size_t workspace_bytes,
+                               flce_dtype dt, hipStream_t stream,
+                               hipEvent_t* events, int64_t n_events);
+
+/*
  * Step 1 alone: the logits of `rows` tokens, z[i * ldz + j] = sum_k
  * h[i, k] W[j, k] in fp32 (MFMA, fp32 accumulation), for 0 <= i < rows,
  * 0 <= j < V.  ldz >= V, in floats; z must be 16-byte aligned and, for the

@@ -8,10 +8,14 @@ from ._lib import (
     EXPORTS,
     FLCE_BF16,
     FLCE_F32,
+    FLCE_STEPS,
     FlceError,
+    HipEvents,
     LIB_PATH,
+    STEP_NAMES,
     ce_rows,
     fwd_bwd,
+    launch_count,
     load,
     logits,
     workspace_bytes,
@@ -21,10 +25,14 @@ __all__ = [
     "EXPORTS",
     "FLCE_BF16",
     "FLCE_F32",
+    "FLCE_STEPS",
     "FlceError",
+    "HipEvents",
     "LIB_PATH",
+    "STEP_NAMES",
     "ce_rows",
     "fwd_bwd",
+    "launch_count",
     "load",
     "logits",
     "workspace_bytes",

@@ -33,10 +33,15 @@ STATUS = {
 EXPORTS = (
     "flce_workspace_bytes",
     "flce_fwd_bwd",
+    "flce_launch_count",
+    "flce_fwd_bwd_timed",
     "flce_logits",
     "flce_ce_rows",
     "flce_status_string",
 )
+
+FLCE_STEPS = 5
+STEP_NAMES = ("logits_gemm", "ce_rows", "loss_sum", "grad_h_gemm", "grad_W_gemm")
 
 _lib = None
 
@@ -63,6 +68,11 @@ def load() -> ctypes.CDLL:
     lib.flce_fwd_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, sz,
                                  ctypes.c_int, vp]
     lib.flce_fwd_bwd.restype = ctypes.c_int
+    lib.flce_launch_count.argtypes = [i64, i64]
+    lib.flce_launch_count.restype = i64
+    lib.flce_fwd_bwd_timed.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, sz,
+                                       ctypes.c_int, vp, vp, i64]
+    lib.flce_fwd_bwd_timed.restype = ctypes.c_int
     lib.flce_logits.argtypes = [vp, vp, i64, i64, i64, vp, i64, ctypes.c_int, vp]
     lib.flce_logits.restype = ctypes.c_int
     lib.flce_ce_rows.argtypes = [vp, i64, vp, i64, i64, ctypes.c_float, vp, i64,
@@ -105,16 +115,56 @@ def workspace_bytes(N: int, H: int, V: int, chunk: int, dtype: torch.dtype) -> i
     return int(load().flce_workspace_bytes(N, H, V, chunk, dt))
 
 
+class HipEvents:
+    """A host array of timing-enabled hipEvent_t handles (HIP runtime calls
+    through ctypes), for flce_fwd_bwd_timed."""
+
+    def __init__(self, n: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                  ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.n = n
+        self.array = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.array[i] = h.value
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        out = ctypes.c_float()
+        if self._hip.hipEventSynchronize(self.array[j]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        if self._hip.hipEventElapsedTime(ctypes.byref(out), self.array[i], self.array[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self) -> None:
+        for i in range(self.n):
+            if self.array[i]:
+                self._hip.hipEventDestroy(self.array[i])
+                self.array[i] = None
+
+
+def launch_count(N: int, chunk: int) -> int:
+    return int(load().flce_launch_count(N, chunk))
+
+
 def fwd_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
             chunk: Optional[int] = None, *,
             loss: Optional[torch.Tensor] = None,
             grad_h: Optional[torch.Tensor] = None,
             grad_W: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None,
+            events: Optional[HipEvents] = None,
             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Mean cross-entropy loss of h W^T against targets, with dloss/dh and
-    dloss/dW, via ``flce_fwd_bwd``.  Returns (loss [] fp32, grad_h like h,
-    grad_W [V, H] fp32).  Buffers may be passed in to avoid allocation."""
+    dloss/dW, via ``flce_fwd_bwd`` (or ``flce_fwd_bwd_timed`` when
+    ``events`` is given).  Returns (loss [] fp32, grad_h like h, grad_W
+    [V, H] fp32).  Buffers may be passed in to avoid allocation."""
     lib = load()
     _need_cuda(h, W, targets)
     if targets.dtype != torch.int32:
@@ -136,10 +186,14 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _need_cuda(loss, grad_h, grad_W, workspace)
-    st = lib.flce_fwd_bwd(h.data_ptr(), W.data_ptr(), targets.data_ptr(), N, H, V, chunk,
-                          loss.data_ptr(), grad_h.data_ptr(), grad_W.data_ptr(),
-                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                          dt, _stream_ptr(dev))
+    args = (h.data_ptr(), W.data_ptr(), targets.data_ptr(), N, H, V, chunk,
+            loss.data_ptr(), grad_h.data_ptr(), grad_W.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            dt, _stream_ptr(dev))
+    if events is None:
+        st = lib.flce_fwd_bwd(*args)
+    else:
+        st = lib.flce_fwd_bwd_timed(*args, events.array, events.n)
     _check(st)
     return loss, grad_h, grad_W
 

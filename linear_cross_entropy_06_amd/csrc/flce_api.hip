@@ -44,11 +44,33 @@ extern "C" size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t 
   return static_cast<size_t>(C) * static_cast<size_t>(V) * 4u;
 }
 
-extern "C" flce_status flce_fwd_bwd(const void* h, const void* W, const int32_t* targets,
-                                    int64_t N, int64_t H, int64_t V, int64_t chunk,
-                                    float* loss, void* grad_h, float* grad_W,
-                                    void* workspace, size_t workspace_bytes, flce_dtype dt,
-                                    hipStream_t stream) {
+extern "C" int64_t flce_launch_count(int64_t N, int64_t chunk) {
+  if (!dims_ok(N) || chunk < 1) return 0;
+  const int64_t C = chunk < N ? chunk : N;
+  return FLCE_STEPS * ((N + C - 1) / C);
+}
+
+namespace {
+
+// Records events[2k] / events[2k+1] around launch k when events != nullptr.
+struct Marks {
+  hipEvent_t* ev;
+  hipStream_t s;
+  int64_t k = 0;
+  void before() {
+    if (ev) (void)hipEventRecord(ev[2 * k], s);
+  }
+  void after() {
+    if (ev) (void)hipEventRecord(ev[2 * k + 1], s);
+    ++k;
+  }
+};
+
+flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, int64_t N,
+                         int64_t H, int64_t V, int64_t chunk, float* loss, void* grad_h,
+                         float* grad_W, void* workspace, size_t workspace_bytes,
+                         flce_dtype dt, hipStream_t stream, hipEvent_t* events,
+                         int64_t n_events) {
   if (!h || !W || !targets || !loss || !grad_h || !grad_W || !workspace)
     return FLCE_ERR_INVALID_ARG;
   if (!dims_ok(N) || !dims_ok(H) || !dims_ok(V) || chunk < 1 || !dtype_ok(dt))
@@ -58,9 +80,11 @@ extern "C" flce_status flce_fwd_bwd(const void* h, const void* W, const int32_t*
       !aligned16(workspace) || (reinterpret_cast<uintptr_t>(targets) & 3u) ||
       (reinterpret_cast<uintptr_t>(loss) & 3u))
     return FLCE_ERR_UNSUPPORTED;
+  if (events && n_events < 2 * flce_launch_count(N, chunk)) return FLCE_ERR_INVALID_ARG;
   const size_t need = flce_workspace_bytes(N, H, V, chunk, dt);
   if (workspace_bytes < need) return FLCE_ERR_WORKSPACE;
 
+  Marks mk{events, stream};
   const int64_t C = chunk < N ? chunk : N;
   const int64_t es = esize(dt);
   const bool bf16 = dt == FLCE_BF16;
@@ -81,33 +105,65 @@ extern "C" flce_status flce_fwd_bwd(const void* h, const void* W, const int32_t*
 
     // 1. Z^T = W . h_c^T, stored as Z[i][j] (row pitch V floats).
     flce::GemmArgs g1{W, H, hc, H, z, V, static_cast<int>(V), rows, static_cast<int>(H), 0};
-    if ((e = gemm(dt, true, true, flce::kStoreF32, vec, g1, stream)) != hipSuccess)
-      return FLCE_ERR_HIP;
+    mk.before();
+    e = gemm(dt, true, true, flce::kStoreF32, vec, g1, stream);
+    mk.after();
+    if (e != hipSuccess) return FLCE_ERR_HIP;
 
     // 2. lse and row losses; Z -> G in place.
-    if ((e = flce::launch_ce_rows(z, V, targets + r0, rows, static_cast<int>(V), inv_n,
-                                  staged, loss_stride, bf16, stream)) != hipSuccess)
-      return FLCE_ERR_HIP;
+    mk.before();
+    e = flce::launch_ce_rows(z, V, targets + r0, rows, static_cast<int>(V), inv_n, staged,
+                             loss_stride, bf16, stream);
+    mk.after();
+    if (e != hipSuccess) return FLCE_ERR_HIP;
 
     // 3. running mean loss.
-    if ((e = flce::launch_loss_sum(staged, loss_stride, rows, inv_n, r0 == 0 ? 1 : 0, loss,
-                                   stream)) != hipSuccess)
-      return FLCE_ERR_HIP;
+    mk.before();
+    e = flce::launch_loss_sum(staged, loss_stride, rows, inv_n, r0 == 0 ? 1 : 0, loss, stream);
+    mk.after();
+    if (e != hipSuccess) return FLCE_ERR_HIP;
 
     // 4. grad_h_c^T = W^T . G^T: A(m = hidden, k = vocab) = W[k][m],
     //    B(n = token, k = vocab) = G[n][k].
     flce::GemmArgs g4{W, H, z, ldg, ghc, H, static_cast<int>(H), rows, static_cast<int>(V), 0};
-    if ((e = gemm(dt, false, true, flce::kStoreOut, vec, g4, stream)) != hipSuccess)
-      return FLCE_ERR_HIP;
+    mk.before();
+    e = gemm(dt, false, true, flce::kStoreOut, vec, g4, stream);
+    mk.after();
+    if (e != hipSuccess) return FLCE_ERR_HIP;
 
     // 5. grad_W^T (+)= h_c^T . G: A(m = hidden, k = token) = h_c[k][m],
     //    B(n = vocab, k = token) = G[k][n].
     flce::GemmArgs g5{hc, H, z, ldg, grad_W, H, static_cast<int>(H), static_cast<int>(V), rows,
                       r0 == 0 ? 0 : 1};
-    if ((e = gemm(dt, false, false, flce::kAccumF32, vec, g5, stream)) != hipSuccess)
-      return FLCE_ERR_HIP;
+    mk.before();
+    e = gemm(dt, false, false, flce::kAccumF32, vec, g5, stream);
+    mk.after();
+    if (e != hipSuccess) return FLCE_ERR_HIP;
   }
   return FLCE_OK;
+}
+
+}  // namespace
+
+extern "C" flce_status flce_fwd_bwd(const void* h, const void* W, const int32_t* targets,
+                                    int64_t N, int64_t H, int64_t V, int64_t chunk,
+                                    float* loss, void* grad_h, float* grad_W,
+                                    void* workspace, size_t workspace_bytes, flce_dtype dt,
+                                    hipStream_t stream) {
+  return fwd_bwd_impl(h, W, targets, N, H, V, chunk, loss, grad_h, grad_W, workspace,
+                      workspace_bytes, dt, stream, nullptr, 0);
+}
+
+extern "C" flce_status flce_fwd_bwd_timed(const void* h, const void* W,
+                                          const int32_t* targets, int64_t N, int64_t H,
+                                          int64_t V, int64_t chunk, float* loss, void* grad_h,
+                                          float* grad_W, void* workspace,
+                                          size_t workspace_bytes, flce_dtype dt,
+                                          hipStream_t stream, hipEvent_t* events,
+                                          int64_t n_events) {
+  if (!events) return FLCE_ERR_INVALID_ARG;
+  return fwd_bwd_impl(h, W, targets, N, H, V, chunk, loss, grad_h, grad_W, workspace,
+                      workspace_bytes, dt, stream, events, n_events);
 }
 
 extern "C" flce_status flce_logits(const void* h, const void* W, int64_t rows, int64_t H,

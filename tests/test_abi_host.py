@@ -36,8 +36,9 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    assert names == sorted(["flce_workspace_bytes", "flce_fwd_bwd", "flce_logits",
-                            "flce_ce_rows", "flce_status_string"])
+    assert names == sorted(["flce_workspace_bytes", "flce_fwd_bwd", "flce_launch_count",
+                            "flce_fwd_bwd_timed", "flce_logits", "flce_ce_rows",
+                            "flce_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -93,6 +94,21 @@ def test_hidden_not_multiple_of_8_is_unsupported(lib, H):
 @pytest.mark.parametrize("field", ["h", "W", "gh", "gW", "ws"])
 def test_misaligned_pointer_is_unsupported(lib, field):
     assert _call(lib, **{field: P + 8}) == UNSUPPORTED
+
+
+def test_launch_count(lib):
+    assert lib.flce_launch_count(8192, 4096) == 10
+    assert lib.flce_launch_count(8192, 3000) == 15
+    assert lib.flce_launch_count(10, 100) == 5
+    assert lib.flce_launch_count(0, 4) == 0 and lib.flce_launch_count(4, 0) == 0
+
+
+def test_timed_entry_checks_event_count(lib):
+    ev = (ctypes.c_void_p * 4)()
+    a = (P, P, P, 4, 8, 5, 2, P, P, P, P, 1 << 20, BF16, None)
+    # 2 chunks -> 10 launches -> 20 events needed
+    assert lib.flce_fwd_bwd_timed(*a, ev, 4) == INVALID
+    assert lib.flce_fwd_bwd_timed(*a, None, 40) == INVALID
 
 
 def test_small_workspace(lib):

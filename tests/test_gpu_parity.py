@@ -319,3 +319,23 @@ def test_out_of_range_target_is_nan_not_a_fault(flce):
     loss, gh, gw = flce.fwd_bwd(h, W, t, 8)
     torch.cuda.synchronize()
     assert math.isnan(float(loss))
+
+
+def test_timed_entry_point_matches(flce):
+    """flce_fwd_bwd_timed computes the same bits and records ordered events."""
+    inp = make_random(600, 64, 1000, dtype="bf16", seed=11)
+    h, W, t = to_device(inp)
+    C = 256
+    L = flce.launch_count(600, C)
+    assert L == 3 * flce.FLCE_STEPS
+    ev = flce.HipEvents(2 * L)
+    say("flce_fwd_bwd_timed")
+    a = tuple(x.clone() for x in flce.fwd_bwd(h, W, t, C))
+    b = flce.fwd_bwd(h, W, t, C, events=ev)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    times = [ev.elapsed_ms(2 * k, 2 * k + 1) for k in range(L)]
+    assert all(x >= 0 for x in times)
+    assert ev.elapsed_ms(0, 2 * L - 1) >= max(times)
+    ev.close()
