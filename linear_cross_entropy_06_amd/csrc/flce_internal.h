@@ -37,6 +37,12 @@ struct GemmArgs {
 hipError_t launch_gemm_bf16(bool a_kc, bool b_kc, int epi, bool vec,
                             const GemmArgs& g, hipStream_t s);
 
+// The same bf16 contraction through the direct-to-LDS pipeline of
+// gemm_bf16_dma.hip; valid when gemm_bf16_dma_supported() holds.
+bool gemm_bf16_dma_supported(bool a_kc, bool b_kc, const GemmArgs& g);
+hipError_t launch_gemm_bf16_dma(bool a_kc, bool b_kc, int epi, const GemmArgs& g,
+                                int m_fastest, hipStream_t s);
+
 // fp32 operands, same index semantics (used by FLCE_F32).
 hipError_t launch_gemm_f32(bool a_kc, bool b_kc, int epi, const GemmArgs& g,
                            hipStream_t s);

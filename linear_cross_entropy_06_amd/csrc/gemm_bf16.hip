@@ -32,6 +32,8 @@
 //    reused from L2 by consecutive tiles.
 #include "flce_internal.h"
 
+#include <stdlib.h>
+
 namespace flce {
 namespace {
 
@@ -339,6 +341,16 @@ hipError_t launch_layout(bool vec, const GemmArgs& g, int m_fastest, hipStream_t
   return launch_t<TileBig, A_KC, B_KC, false, EPI, OutT>(g, m_fastest, s);
 }
 
+// The direct-to-LDS pipeline is the default; FLCE_GEMM_GENERIC=1 in the
+// environment forces the register-staged kernel (for A/B comparisons).
+bool dma_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("FLCE_GEMM_GENERIC");
+    return !(e && e[0] == '1');
+  }();
+  return on;
+}
+
 }  // namespace
 
 hipError_t launch_gemm_bf16(bool a_kc, bool b_kc, int epi, bool vec,
@@ -347,6 +359,8 @@ hipError_t launch_gemm_bf16(bool a_kc, bool b_kc, int epi, bool vec,
   // Walk the dimension of the smaller operand fastest, so that a panel of
   // the larger operand stays in L2 across consecutive tiles.
   const int m_fastest = g.M < g.N ? 1 : 0;
+  if (vec && dma_enabled() && gemm_bf16_dma_supported(a_kc, b_kc, g))
+    return launch_gemm_bf16_dma(a_kc, b_kc, epi, g, m_fastest, s);
   if (a_kc && b_kc && epi == kStoreF32)       // logits
     return launch_layout<true, true, kStoreF32, float>(vec, g, m_fastest, s);
   if (!a_kc && b_kc && epi == kStoreOut)      // grad_h (bf16 out)

@@ -1,0 +1,333 @@
+// bf16 MFMA contraction with a direct-to-LDS operand pipeline (gfx950).
+//
+// Same contract as the generic kernel in gemm_bf16.hip (D[m][n] =
+// sum_k A(m,k) B(n,k), stored as out[n * ldo + m]) for the shapes the
+// loss head runs at scale: K a multiple of 32, every contiguous extent and
+// leading dimension a multiple of 8 elements, 16-byte aligned bases.
+//
+// CDNA4 design:
+//  * 256x256 output tile per 256-thread workgroup; each wave64 owns a
+//    128x128 quarter = 4x4 v_mfma_f32_32x32x16_bf16 blocks (256 fp32
+//    accumulators per lane, one wave per SIMD).
+//  * Operand tiles move HBM/L2 -> LDS with global_load_lds_dwordx4 (no
+//    VGPR staging) into two 64-wide K slabs (2 x 64 KiB): slab kt + 1 is
+//    requested when the multiplication of slab kt starts.  A 64-wide slab
+//    makes every k-contiguous row segment a whole 128-byte line, so the
+//    cache sees one request per line.
+//  * Each operand stays in its memory layout in LDS:
+//      k-contiguous  tile [row][64 k]   128 B rows, fragment = ds_read_b128
+//      m-contiguous  tile [k][256 rows] 512 B rows, fragment = two
+//                    ds_read_b64_tr_b16: a 16-lane group reads a 4(k) x 16(m)
+//                    block as sixteen 8-byte pieces and each lane receives
+//                    4 consecutive k of one m, i.e. an MFMA operand slice.
+//    16-byte chunks are XOR-swizzled per row (the DMA source address is
+//    permuted to match) so fragment reads hit distinct LDS banks.
+//  * MFMA operands are double-buffered in registers: the fragments of the
+//    next 16-wide k step are read while the current step's 16 MFMAs run.
+//  * One barrier per slab, placed in the middle of the slab's last k step
+//    so the MFMAs queued before it cover the wait.
+//  * Rows beyond M/N are loaded from a clamped (valid) address and their
+//    results are never stored.
+#include "flce_internal.h"
+
+namespace flce {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+constexpr int kBM = 256, kBN = 256, kBK = 64, kStages = 2;
+constexpr int kKSteps = kBK / 16;              // MFMA k steps per slab
+constexpr int kTileBytes = 256 * kBK * 2;      // one operand slab: 32 KiB
+constexpr int kStageBytes = 2 * kTileBytes;    // A then B: 64 KiB
+constexpr int kDmaPerOp = kTileBytes / (256 * 16);  // 8 DMA instructions per thread
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  const int per = total / kXcds;
+  if (b >= per * kXcds) return b;
+  return (b % kXcds) * per + b / kXcds;
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt left open).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// Workgroup barrier without a memory fence (a fence would wait for every
+// outstanding DMA).  The signal fences only stop the compiler from moving
+// memory operations across the barrier; the hardware waits are explicit.
+__device__ __forceinline__ void block_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Per-thread DMA sources of one operand slab (kDmaPerOp 16-byte pieces).
+// Instruction i of wave w fills 1 KiB block b = kDmaPerOp * w + i of the
+// slab; lane l of that instruction lands at byte 16 * l of the block.
+template <bool KC>
+struct DmaOperand {
+  const char* src[kDmaPerOp];  // byte address of the piece for k slab 0
+  int64_t kstep;               // bytes to advance per k slab
+
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int row0,
+                                       int rows_total, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kDmaPerOp; ++i) {
+      const int b = kDmaPerOp * wave + i;
+      int64_t elem;
+      if constexpr (KC) {
+        // 8 rows of 64 k (128 B) per block; 8 chunks per row.
+        const int row = 8 * b + (lane >> 3);
+        const int c = (lane & 7) ^ (row & 7);
+        int grow = row0 + row;
+        grow = grow < rows_total ? grow : rows_total - 1;
+        elem = (int64_t)grow * ld + 8 * c;
+      } else {
+        // 2 k-rows of 256 m (512 B) per block; 32 chunks per row.
+        const int krow = 2 * b + (lane >> 5);
+        const int c = (lane & 31) ^ (2 * (krow & 3));
+        int gm = row0 + 8 * c;
+        gm = gm <= rows_total - 8 ? gm : rows_total - 8;
+        elem = (int64_t)krow * ld + gm;
+      }
+      src[i] = reinterpret_cast<const char*>(base + elem);
+    }
+    kstep = KC ? (int64_t)kBK * 2 : (int64_t)kBK * ld * 2;
+  }
+
+  __device__ __forceinline__ void issue(int kt, char* slab, int wave) const {
+#pragma unroll
+    for (int i = 0; i < kDmaPerOp; ++i) {
+      const int b = kDmaPerOp * wave + i;
+      __builtin_amdgcn_global_load_lds((gbl_void*)(src[i] + kt * kstep),
+                                       (lds_void*)(slab + 1024 * b), 16, 0, 0);
+    }
+  }
+};
+
+// Fragment reads of one operand for one 16-wide k step: 4 blocks of 32 rows.
+template <bool KC>
+struct FragOperand {
+  uint32_t off[4];  // per-lane byte offsets inside a slab (see init)
+
+  __device__ __forceinline__ void init(int wrow0, int lane) {
+    if constexpr (KC) {
+      // row = wrow0 + 32 i + (lane & 31); chunk = 2 kk + (lane >> 5).
+      const int row = wrow0 + (lane & 31);
+      const int x = row & 7;
+      const int h = lane >> 5;
+#pragma unroll
+      for (int kk = 0; kk < kKSteps; ++kk) off[kk] = row * 128 + (((2 * kk + h) ^ x) * 16);
+    } else {
+      // 16-lane group G reads k rows 8 (G >> 1) + 4 t + (j >> 2) and
+      // m = 16 (G & 1) + 4 (j & 3) .. + 3 of each 32-row block.
+      const int G = lane >> 4, j = lane & 15;
+      const int krow = 8 * (G >> 1) + (j >> 2);
+      const int x = 2 * (krow & 3);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = wrow0 + 32 * i + 16 * (G & 1) + 4 * (j & 3);
+        off[i] = krow * 512 + (((m >> 3) ^ x) * 16) + 8 * ((m >> 2) & 1);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void read(const char* slab, int kk, bf16x8 (&f)[4]) const {
+    if constexpr (KC) {
+      const char* p = slab + off[kk];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        f[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p + 4096 * i));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const char* p = slab + off[i] + kk * 8192;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 2048));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        f[i] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+      }
+    }
+  }
+};
+
+// 32x32x16 MFMAs over the 4x4 blocks, rows i0 .. i1 - 1 of the block grid.
+template <int I0, int I1>
+__device__ __forceinline__ void mma(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
+                                    const bf16x8 (&b)[4]) {
+#pragma unroll
+  for (int i = I0; i < I1; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+template <bool A_KC, bool B_KC, int EPI, typename OutT>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_bf16_dma_kernel(GemmArgs g, int m_fastest) {
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+
+  const int tiles_m = (g.M + kBM - 1) / kBM;
+  const int tiles_n = (g.N + kBN - 1) / kBN;
+  const int t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+  int tmi, tni;
+  if (m_fastest) {
+    tmi = t % tiles_m;
+    tni = t / tiles_m;
+  } else {
+    tmi = t / tiles_n;
+    tni = t % tiles_n;
+  }
+  const int m0 = tmi * kBM, n0 = tni * kBN;
+
+  DmaOperand<A_KC> da;
+  DmaOperand<B_KC> db;
+  da.init(static_cast<const uint16_t*>(g.A), g.lda, m0, g.M, wave, lane);
+  db.init(static_cast<const uint16_t*>(g.B), g.ldb, n0, g.N, wave, lane);
+  FragOperand<A_KC> fa;
+  FragOperand<B_KC> fb;
+  fa.init(wm * 128, lane);
+  fb.init(wn * 128, lane);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int KT = g.K / kBK;
+  // Prologue: slab 0 into stage 0.
+  da.issue(0, smem, wave);
+  db.issue(0, smem + kTileBytes, wave);
+  wait_vmcnt<0>();
+  block_barrier();
+
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  fa.read(smem, 0, a0);
+  fb.read(smem + kTileBytes, 0, b0);
+
+  for (int kt = 0; kt < KT; ++kt) {
+    char* slab = smem + (kt & 1) * kStageBytes;
+    char* nxt = smem + ((kt + 1) & 1) * kStageBytes;
+    // The other stage was last read in slab kt - 1, before the barrier that
+    // ended it: refill it with slab kt + 1 while slab kt is multiplied.
+    if (kt + 1 < KT) {
+      da.issue(kt + 1, nxt, wave);
+      db.issue(kt + 1, nxt + kTileBytes, wave);
+    }
+    fa.read(slab, 1, a1);
+    fb.read(slab + kTileBytes, 1, b1);
+    mma<0, 4>(acc, a0, b0);
+    fa.read(slab, 2, a0);
+    fb.read(slab + kTileBytes, 2, b0);
+    mma<0, 4>(acc, a1, b1);
+    fa.read(slab, 3, a1);
+    fb.read(slab + kTileBytes, 3, b1);
+    mma<0, 4>(acc, a0, b0);
+    mma<0, 2>(acc, a1, b1);
+    // slab kt + 1 landed for every wave; every read of slab kt is done
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    block_barrier();
+    if (kt + 1 < KT) {
+      fa.read(nxt, 0, a0);
+      fb.read(nxt + kTileBytes, 0, b0);
+    }
+    mma<2, 4>(acc, a1, b1);
+  }
+
+  // Epilogue.  Accumulator r of lane l in block (i, j) is
+  // D[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32] of that 32x32 block.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 128 + j * 32 + (lane & 31);
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
+        if (m >= g.M) continue;  // M % 8 == 0: a run of 4 is all in or all out
+        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                         acc[i][j][4 * q + 3]};
+        const int64_t off = (int64_t)n * g.ldo + m;
+        if constexpr (EPI == kStoreOut && sizeof(OutT) == 2) {
+          u32x2 w;
+          w[0] = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
+          w[1] = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + off) = w;
+        } else {
+          float* o = static_cast<float*>(g.out) + off;
+          f32x4 w = v;
+          if (EPI == kAccumF32 && g.beta) w += *reinterpret_cast<const f32x4*>(o);
+          *reinterpret_cast<f32x4*>(o) = w;
+        }
+      }
+    }
+  }
+}
+
+template <bool A_KC, bool B_KC, int EPI, typename OutT>
+hipError_t launch_dma(const GemmArgs& g, int m_fastest, hipStream_t s) {
+  const int tiles = ((g.M + kBM - 1) / kBM) * ((g.N + kBN - 1) / kBN);
+  hipLaunchKernelGGL((gemm_bf16_dma_kernel<A_KC, B_KC, EPI, OutT>), dim3(tiles), dim3(256), 0,
+                     s, g, m_fastest);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_bf16_dma_supported(bool a_kc, bool b_kc, const GemmArgs& g) {
+  if (g.K <= 0 || g.K % kBK != 0 || g.M <= 0 || g.N <= 0) return false;
+  if (g.M % 8 != 0 || g.N % 8 != 0) return false;
+  if ((g.lda % 8) || (g.ldb % 8) || (g.ldo % 4)) return false;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B) |
+                       reinterpret_cast<uintptr_t>(g.out);
+  if (al & 15u) return false;
+  (void)a_kc;
+  (void)b_kc;
+  return true;
+}
+
+hipError_t launch_gemm_bf16_dma(bool a_kc, bool b_kc, int epi, const GemmArgs& g, int m_fastest,
+                                hipStream_t s) {
+  if (a_kc && b_kc && epi == kStoreF32)
+    return launch_dma<true, true, kStoreF32, float>(g, m_fastest, s);
+  if (!a_kc && b_kc && epi == kStoreOut)
+    return launch_dma<false, true, kStoreOut, uint16_t>(g, m_fastest, s);
+  if (!a_kc && !b_kc && epi == kAccumF32)
+    return launch_dma<false, false, kAccumF32, float>(g, m_fastest, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace flce
