@@ -105,6 +105,8 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
 
     // 1. Z^T = W . h_c^T, stored as Z[i][j] (row pitch V floats).
     flce::GemmArgs g1{W, H, hc, H, z, V, static_cast<int>(V), rows, static_cast<int>(H), 0};
+    g1.group_m = 4;
+    g1.stagger = 37;
     mk.before();
     e = gemm(dt, true, true, flce::kStoreF32, vec, g1, stream);
     mk.after();
@@ -126,6 +128,7 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
     // 4. grad_h_c^T = W^T . G^T: A(m = hidden, k = vocab) = W[k][m],
     //    B(n = token, k = vocab) = G[n][k].
     flce::GemmArgs g4{W, H, z, ldg, ghc, H, static_cast<int>(H), rows, static_cast<int>(V), 0};
+    g4.group_m = 4;
     mk.before();
     e = gemm(dt, false, true, flce::kStoreOut, vec, g4, stream);
     mk.after();
@@ -135,6 +138,8 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
     //    B(n = vocab, k = token) = G[k][n].
     flce::GemmArgs g5{hc, H, z, ldg, grad_W, H, static_cast<int>(H), static_cast<int>(V), rows,
                       r0 == 0 ? 0 : 1};
+    g5.group_m = 4;
+    g5.stagger = 37;
     mk.before();
     e = gemm(dt, false, false, flce::kAccumF32, vec, g5, stream);
     mk.after();

@@ -28,6 +28,12 @@ struct GemmArgs {
   int64_t ldo;
   int M, N, K;
   int beta;
+  // Tile order (direct-to-LDS kernel): tiles are walked in groups of
+  // group_m row panels (m fastest inside a group); 0 picks a default.
+  int group_m = 0;
+  // K-start rotation per tile group: group g starts its K walk at slab
+  // (g * stagger) mod (K / 64); 0 disables it.
+  int stagger = 0;
 };
 
 // bf16 operands, MFMA 32x32x16, fp32 accumulation.  `vec` selects the
@@ -41,7 +47,7 @@ hipError_t launch_gemm_bf16(bool a_kc, bool b_kc, int epi, bool vec,
 // gemm_bf16_dma.hip; valid when gemm_bf16_dma_supported() holds.
 bool gemm_bf16_dma_supported(bool a_kc, bool b_kc, const GemmArgs& g);
 hipError_t launch_gemm_bf16_dma(bool a_kc, bool b_kc, int epi, const GemmArgs& g,
-                                int m_fastest, hipStream_t s);
+                                hipStream_t s);
 
 // fp32 operands, same index semantics (used by FLCE_F32).
 hipError_t launch_gemm_f32(bool a_kc, bool b_kc, int epi, const GemmArgs& g,

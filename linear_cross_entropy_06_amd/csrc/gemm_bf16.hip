@@ -360,7 +360,7 @@ hipError_t launch_gemm_bf16(bool a_kc, bool b_kc, int epi, bool vec,
   // the larger operand stays in L2 across consecutive tiles.
   const int m_fastest = g.M < g.N ? 1 : 0;
   if (vec && dma_enabled() && gemm_bf16_dma_supported(a_kc, b_kc, g))
-    return launch_gemm_bf16_dma(a_kc, b_kc, epi, g, m_fastest, s);
+    return launch_gemm_bf16_dma(a_kc, b_kc, epi, g, s);
   if (a_kc && b_kc && epi == kStoreF32)       // logits
     return launch_layout<true, true, kStoreF32, float>(vec, g, m_fastest, s);
   if (!a_kc && b_kc && epi == kStoreOut)      // grad_h (bf16 out)

@@ -23,7 +23,11 @@
 //    16-byte chunks are XOR-swizzled per row (the DMA source address is
 //    permuted to match) so fragment reads hit distinct LDS banks.
 //  * MFMA operands are double-buffered in registers: the fragments of the
-//    next 16-wide k step are read while the current step's 16 MFMAs run.
+//    next 16-wide k step are read while the current step's 16 MFMAs run;
+//    the next slab's DMA requests are interleaved one per MFMA.
+//  * Tiles are walked in groups of 4 row panels (each XCD's ~32 concurrent
+//    tiles form a 4 x 8 block sharing operand slabs in L2); optionally each
+//    group starts its K walk at a rotated slab to spread L2 channel load.
 //  * One barrier per slab, placed in the middle of the slab's last k step
 //    so the MFMAs queued before it cover the wait.
 //  * Rows beyond M/N are loaded from a clamped (valid) address and their
@@ -117,7 +121,12 @@ struct DmaOperand {
     kstep = KC ? (int64_t)kBK * 2 : (int64_t)kBK * ld * 2;
   }
 
+  int start = 0;     // first K slab of this tile (rotation)
+  int kt_total = 1;  // K slabs
+
   __device__ __forceinline__ void issue(int kt, char* slab, int wave) const {
+    kt += start;
+    if (kt >= kt_total) kt -= kt_total;
 #pragma unroll
     for (int i = 0; i < kDmaPerOp; ++i) {
       const int b = kDmaPerOp * wave + i;
@@ -187,7 +196,7 @@ __device__ __forceinline__ void mma(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
 
 template <bool A_KC, bool B_KC, int EPI, typename OutT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_bf16_dma_kernel(GemmArgs g, int m_fastest) {
+gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
 
   const int tid = threadIdx.x;
@@ -198,14 +207,17 @@ gemm_bf16_dma_kernel(GemmArgs g, int m_fastest) {
   const int tiles_m = (g.M + kBM - 1) / kBM;
   const int tiles_n = (g.N + kBN - 1) / kBN;
   const int t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-  int tmi, tni;
-  if (m_fastest) {
-    tmi = t % tiles_m;
-    tni = t / tiles_m;
-  } else {
-    tmi = t / tiles_n;
-    tni = t % tiles_n;
-  }
+  // Grouped order: group = group_m row panels x all column panels, row
+  // panel fastest, so the ~32 tiles an XCD runs at once form a compact
+  // block and share operand slabs in its L2.
+  const int gm = group_m;
+  const int per_group = gm * tiles_n;
+  const int grp = t / per_group;
+  const int first_m = grp * gm;
+  const int gsize = min(tiles_m - first_m, gm);
+  const int r = t - grp * per_group;
+  const int tmi = first_m + r % gsize;
+  const int tni = r / gsize;
   const int m0 = tmi * kBM, n0 = tni * kBN;
 
   DmaOperand<A_KC> da;
@@ -226,6 +238,8 @@ gemm_bf16_dma_kernel(GemmArgs g, int m_fastest) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int KT = g.K / kBK;
+  da.kt_total = db.kt_total = KT;
+  da.start = db.start = g.stagger > 0 ? (int)(((unsigned)grp * (unsigned)g.stagger) % (unsigned)KT) : 0;
   // Prologue: slab 0 into stage 0.
   da.issue(0, smem, wave);
   db.issue(0, smem + kTileBytes, wave);
@@ -240,14 +254,23 @@ gemm_bf16_dma_kernel(GemmArgs g, int m_fastest) {
     char* slab = smem + (kt & 1) * kStageBytes;
     char* nxt = smem + ((kt + 1) & 1) * kStageBytes;
     // The other stage was last read in slab kt - 1, before the barrier that
-    // ended it: refill it with slab kt + 1 while slab kt is multiplied.
-    if (kt + 1 < KT) {
-      da.issue(kt + 1, nxt, wave);
-      db.issue(kt + 1, nxt + kTileBytes, wave);
-    }
+    // ended it: refill it with slab kt + 1 while slab kt is multiplied.  The
+    // last slab re-requests itself (L2 hits, never read) so that the loop
+    // body stays one basic block the scheduler can interleave.
+    const int kn = kt + 1 < KT ? kt + 1 : kt;
     fa.read(slab, 1, a1);
     fb.read(slab + kTileBytes, 1, b1);
+    da.issue(kn, nxt, wave);
+    db.issue(kn, nxt + kTileBytes, wave);
     mma<0, 4>(acc, a0, b0);
+    // Spread the 16 DMA requests over the first 16 MFMAs instead of one
+    // burst: one DMA after each MFMA, after the 8 fragment reads.
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int q = 0; q < 2 * kDmaPerOp; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
     fa.read(slab, 2, a0);
     fb.read(slab + kTileBytes, 2, b0);
     mma<0, 4>(acc, a1, b1);
@@ -259,10 +282,8 @@ gemm_bf16_dma_kernel(GemmArgs g, int m_fastest) {
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     block_barrier();
-    if (kt + 1 < KT) {
-      fa.read(nxt, 0, a0);
-      fb.read(nxt + kTileBytes, 0, b0);
-    }
+    fa.read(nxt, 0, a0);
+    fb.read(nxt + kTileBytes, 0, b0);
     mma<2, 4>(acc, a1, b1);
   }
 
@@ -298,10 +319,13 @@ gemm_bf16_dma_kernel(GemmArgs g, int m_fastest) {
 }
 
 template <bool A_KC, bool B_KC, int EPI, typename OutT>
-hipError_t launch_dma(const GemmArgs& g, int m_fastest, hipStream_t s) {
-  const int tiles = ((g.M + kBM - 1) / kBM) * ((g.N + kBN - 1) / kBN);
-  hipLaunchKernelGGL((gemm_bf16_dma_kernel<A_KC, B_KC, EPI, OutT>), dim3(tiles), dim3(256), 0,
-                     s, g, m_fastest);
+hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
+  const int tiles_m = (g.M + kBM - 1) / kBM;
+  const int tiles_n = (g.N + kBN - 1) / kBN;
+  int gm = g.group_m > 0 ? g.group_m : 4;
+  if (gm > tiles_m) gm = tiles_m;
+  hipLaunchKernelGGL((gemm_bf16_dma_kernel<A_KC, B_KC, EPI, OutT>), dim3(tiles_m * tiles_n),
+                     dim3(256), 0, s, g, gm);
   return hipGetLastError();
 }
 
@@ -319,14 +343,13 @@ bool gemm_bf16_dma_supported(bool a_kc, bool b_kc, const GemmArgs& g) {
   return true;
 }
 
-hipError_t launch_gemm_bf16_dma(bool a_kc, bool b_kc, int epi, const GemmArgs& g, int m_fastest,
+hipError_t launch_gemm_bf16_dma(bool a_kc, bool b_kc, int epi, const GemmArgs& g,
                                 hipStream_t s) {
-  if (a_kc && b_kc && epi == kStoreF32)
-    return launch_dma<true, true, kStoreF32, float>(g, m_fastest, s);
+  if (a_kc && b_kc && epi == kStoreF32) return launch_dma<true, true, kStoreF32, float>(g, s);
   if (!a_kc && b_kc && epi == kStoreOut)
-    return launch_dma<false, true, kStoreOut, uint16_t>(g, m_fastest, s);
+    return launch_dma<false, true, kStoreOut, uint16_t>(g, s);
   if (!a_kc && !b_kc && epi == kAccumF32)
-    return launch_dma<false, false, kAccumF32, float>(g, m_fastest, s);
+    return launch_dma<false, false, kAccumF32, float>(g, s);
   return hipErrorInvalidValue;
 }
 
