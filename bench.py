@@ -38,7 +38,8 @@ PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "llama3_8b_head"
 GEMM_STEPS = ("logits_gemm", "grad_h_gemm", "grad_W_gemm")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3_8b_head.md")
-KERNEL_SOURCES = ("gemm_bf16.hip", "ce_rows.hip", "flce_api.hip", "flce_internal.h")
+KERNEL_SOURCES = ("gemm_bf16.hip", "gemm_bf16_dma.hip", "ce_rows.hip", "flce_api.hip",
+                  "flce_internal.h")
 
 
 def parse_args():
@@ -50,7 +51,10 @@ def parse_args():
     p.add_argument("--chunk", type=int, default=0, help="token chunk (default: workload's)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    p.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="first run one elementwise fp32 copy of this many MiB (a kernel of "
+                        "known traffic, used to scale FETCH_SIZE/WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -142,6 +146,15 @@ def main() -> int:
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     L = flce.launch_count(N, C)
     events = [flce.HipEvents(2 * L) for _ in range(args.steps)]
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.randn(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)   # reads n*4 bytes, writes n*4 bytes
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         flce.fwd_bwd(h, W, t, C, loss=loss, grad_h=gh, grad_W=gw, workspace=ws)
