@@ -48,7 +48,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef const __attribute__((address_space(1))) void gbl_void;
 
-constexpr int kBM = 256, kBN = 256, kBK = 64, kStages = 2;
+constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kKSteps = kBK / 16;              // MFMA k steps per slab
 constexpr int kTileBytes = 256 * kBK * 2;      // one operand slab: 32 KiB
 constexpr int kStageBytes = 2 * kTileBytes;    // A then B: 64 KiB
@@ -197,7 +197,12 @@ __device__ __forceinline__ void mma(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
 template <bool A_KC, bool B_KC, int EPI, typename OutT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
-  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
+  // Two distinct LDS objects, one per stage: with the loop unrolled by two,
+  // every DMA and every fragment read names its stage statically, so the
+  // compiler can tell that the reads of one stage never alias the DMA into
+  // the other and does not wait for the DMA before reading.
+  __shared__ __attribute__((aligned(1024))) char stage0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char stage1[kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -241,36 +246,29 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
   da.kt_total = db.kt_total = KT;
   da.start = db.start = g.stagger > 0 ? (int)(((unsigned)grp * (unsigned)g.stagger) % (unsigned)KT) : 0;
   // Prologue: slab 0 into stage 0.
-  da.issue(0, smem, wave);
-  db.issue(0, smem + kTileBytes, wave);
+  da.issue(0, stage0, wave);
+  db.issue(0, stage0 + kTileBytes, wave);
   wait_vmcnt<0>();
   block_barrier();
 
   bf16x8 a0[4], b0[4], a1[4], b1[4];
-  fa.read(smem, 0, a0);
-  fb.read(smem + kTileBytes, 0, b0);
+  fa.read(stage0, 0, a0);
+  fb.read(stage0 + kTileBytes, 0, b0);
 
-  for (int kt = 0; kt < KT; ++kt) {
-    char* slab = smem + (kt & 1) * kStageBytes;
-    char* nxt = smem + ((kt + 1) & 1) * kStageBytes;
-    // The other stage was last read in slab kt - 1, before the barrier that
-    // ended it: refill it with slab kt + 1 while slab kt is multiplied.  The
-    // last slab re-requests itself (L2 hits, never read) so that the loop
-    // body stays one basic block the scheduler can interleave.
+  // LDS fragment reads per k step (ds_read_b128 per 32-row block, or two
+  // ds_read_b64_tr_b16 for m-contiguous operands).
+  constexpr int kReads = (A_KC ? 4 : 8) + (B_KC ? 4 : 8);
+  // One slab: multiply `slab` while the DMA refills `nxt` with slab kt + 1
+  // (`nxt` was last read in slab kt - 1, before the barrier that ended it).
+  // The last slab re-requests itself (L2 hits, never read) so the body
+  // stays one basic block.
+  auto slab_step = [&](int kt, char* slab, char* nxt) __attribute__((always_inline)) {
     const int kn = kt + 1 < KT ? kt + 1 : kt;
     fa.read(slab, 1, a1);
     fb.read(slab + kTileBytes, 1, b1);
     da.issue(kn, nxt, wave);
     db.issue(kn, nxt + kTileBytes, wave);
     mma<0, 4>(acc, a0, b0);
-    // Spread the 16 DMA requests over the first 16 MFMAs instead of one
-    // burst: one DMA after each MFMA, after the 8 fragment reads.
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int q = 0; q < 2 * kDmaPerOp; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
     fa.read(slab, 2, a0);
     fb.read(slab + kTileBytes, 2, b0);
     mma<0, 4>(acc, a1, b1);
@@ -278,14 +276,38 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
     fb.read(slab + kTileBytes, 3, b1);
     mma<0, 4>(acc, a0, b0);
     mma<0, 2>(acc, a1, b1);
+    // Issue order: each k step first requests all fragments of the next
+    // step, then runs its 16 MFMAs; the first step's MFMAs alternate with
+    // the 16 DMA requests of the next slab.
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+#pragma unroll
+    for (int q = 0; q < 2 * kDmaPerOp; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     // slab kt + 1 landed for every wave; every read of slab kt is done
+    __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     block_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     fa.read(nxt, 0, a0);
     fb.read(nxt + kTileBytes, 0, b0);
     mma<2, 4>(acc, a1, b1);
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
+  };
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    slab_step(kt, stage0, stage1);
+    slab_step(kt + 1, stage1, stage0);
   }
+  if (kt < KT) slab_step(kt, stage0, stage1);
 
   // Epilogue.  Accumulator r of lane l in block (i, j) is
   // D[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32] of that 32x32 block.
