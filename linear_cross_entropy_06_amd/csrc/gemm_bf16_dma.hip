@@ -9,11 +9,16 @@
 //  * 256x256 output tile per 256-thread workgroup; each wave64 owns a
 //    128x128 quarter = 4x4 v_mfma_f32_32x32x16_bf16 blocks (256 fp32
 //    accumulators per lane, one wave per SIMD).
-//  * Operand tiles move HBM/L2 -> LDS with global_load_lds_dwordx4 (no
-//    VGPR staging) into two 64-wide K slabs (2 x 64 KiB): slab kt + 1 is
-//    requested when the multiplication of slab kt starts.  A 64-wide slab
-//    makes every k-contiguous row segment a whole 128-byte line, so the
-//    cache sees one request per line.
+//  * Operand tiles move L2 -> LDS with buffer_load_dwordx4 ... lds (no VGPR
+//    staging).  A buffer (not global) load keeps the compiler's wait-count
+//    model exact: it counts these requests on vmcnt only, so fragment reads
+//    wait on partial lgkmcnt values instead of draining every LDS read.
+//  * K advances in 64-wide slabs; an operand's slab is one 32 KiB tile.  LDS
+//    holds a ring of five tile slots (160 KiB): while slab kt is multiplied,
+//    B of slab kt+1 and A of slab kt+2 stream into the two slots that slab
+//    kt-1 freed.  So every request has one to two slabs of MFMA work to
+//    land in, and the 16 requests per thread are spread over the slab's
+//    first three k steps (6/5/5) instead of bursting.
 //  * Each operand stays in its memory layout in LDS:
 //      k-contiguous  tile [row][64 k]   128 B rows, fragment = ds_read_b128
 //      m-contiguous  tile [k][256 rows] 512 B rows, fragment = two
@@ -23,8 +28,7 @@
 //    16-byte chunks are XOR-swizzled per row (the DMA source address is
 //    permuted to match) so fragment reads hit distinct LDS banks.
 //  * MFMA operands are double-buffered in registers: the fragments of the
-//    next 16-wide k step are read while the current step's 16 MFMAs run;
-//    the next slab's DMA requests are interleaved one per MFMA.
+//    next 16-wide k step are read while the current step's 16 MFMAs run.
 //  * Tiles are walked in groups of 4 row panels (each XCD's ~32 concurrent
 //    tiles form a 4 x 8 block sharing operand slabs in L2); optionally each
 //    group starts its K walk at a rotated slab to spread L2 channel load.
@@ -46,14 +50,18 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef const __attribute__((address_space(1))) void gbl_void;
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kKSteps = kBK / 16;              // MFMA k steps per slab
 constexpr int kTileBytes = 256 * kBK * 2;      // one operand slab: 32 KiB
-constexpr int kStageBytes = 2 * kTileBytes;    // A then B: 64 KiB
+constexpr int kSlots = 5;                      // LDS ring of operand tiles: 160 KiB
 constexpr int kDmaPerOp = kTileBytes / (256 * 16);  // 8 DMA instructions per thread
 constexpr int kXcds = 8;
+// Buffer resource for the operand loads: raw (stride 0) addressing with a
+// 2 GiB range (every piece offset is below 64 rows x the leading dimension,
+// checked by gemm_bf16_dma_supported) and the dword data format.
+constexpr int kBufferRange = 0x7fffffff;
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ int xcd_remap(int b, int total) {
   const int per = total / kXcds;
@@ -89,14 +97,20 @@ __device__ __forceinline__ void block_barrier() {
 
 // Per-thread DMA sources of one operand slab (kDmaPerOp 16-byte pieces).
 // Instruction i of wave w fills 1 KiB block b = kDmaPerOp * w + i of the
-// slab; lane l of that instruction lands at byte 16 * l of the block.
+// slab; lane l of that instruction lands at byte 16 * l of the block.  The
+// pieces are addressed as 32-bit offsets from a per-tile panel base, which
+// a buffer resource turns into loads.
 template <bool KC>
 struct DmaOperand {
-  const char* src[kDmaPerOp];  // byte address of the piece for k slab 0
+  const char* base;            // panel origin: first row (kc) or first m (mc), k slab 0
+  uint32_t voff[kDmaPerOp];    // per-lane byte offset of each piece from base
   int64_t kstep;               // bytes to advance per k slab
+  int start = 0;               // first K slab of this tile (rotation)
+  int kt_total = 1;            // K slabs
 
-  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int row0,
+  __device__ __forceinline__ void init(const uint16_t* ptr, int64_t ld, int row0,
                                        int rows_total, int wave, int lane) {
+    base = reinterpret_cast<const char*>(ptr + (KC ? (int64_t)row0 * ld : (int64_t)row0));
 #pragma unroll
     for (int i = 0; i < kDmaPerOp; ++i) {
       const int b = kDmaPerOp * wave + i;
@@ -107,31 +121,31 @@ struct DmaOperand {
         const int c = (lane & 7) ^ (row & 7);
         int grow = row0 + row;
         grow = grow < rows_total ? grow : rows_total - 1;
-        elem = (int64_t)grow * ld + 8 * c;
+        elem = (int64_t)(grow - row0) * ld + 8 * c;
       } else {
         // 2 k-rows of 256 m (512 B) per block; 32 chunks per row.
         const int krow = 2 * b + (lane >> 5);
         const int c = (lane & 31) ^ (2 * (krow & 3));
         int gm = row0 + 8 * c;
         gm = gm <= rows_total - 8 ? gm : rows_total - 8;
-        elem = (int64_t)krow * ld + gm;
+        elem = (int64_t)krow * ld + (gm - row0);
       }
-      src[i] = reinterpret_cast<const char*>(base + elem);
+      voff[i] = (uint32_t)(elem * 2);
     }
     kstep = KC ? (int64_t)kBK * 2 : (int64_t)kBK * ld * 2;
   }
 
-  int start = 0;     // first K slab of this tile (rotation)
-  int kt_total = 1;  // K slabs
-
-  __device__ __forceinline__ void issue(int kt, char* slab, int wave) const {
+  // Request slab kt (before rotation) into `slot`.
+  __device__ __forceinline__ void issue(int kt, char* slot, int wave) const {
     kt += start;
     if (kt >= kt_total) kt -= kt_total;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(base + kt * kstep), (short)0, kBufferRange, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < kDmaPerOp; ++i) {
       const int b = kDmaPerOp * wave + i;
-      __builtin_amdgcn_global_load_lds((gbl_void*)(src[i] + kt * kstep),
-                                       (lds_void*)(slab + 1024 * b), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + 1024 * b), 16, voff[i], 0,
+                                               0, 0);
     }
   }
 };
@@ -197,12 +211,16 @@ __device__ __forceinline__ void mma(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
 template <bool A_KC, bool B_KC, int EPI, typename OutT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
-  // Two distinct LDS objects, one per stage: with the loop unrolled by two,
-  // every DMA and every fragment read names its stage statically, so the
-  // compiler can tell that the reads of one stage never alias the DMA into
-  // the other and does not wait for the DMA before reading.
-  __shared__ __attribute__((aligned(1024))) char stage0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char stage1[kStageBytes];
+  // Five distinct LDS objects, one per ring slot: every DMA and every
+  // fragment read names its slot statically (the K loop is unrolled by
+  // five), so the compiler can tell which reads a DMA may overwrite and
+  // never waits for an unrelated one.
+  __shared__ __attribute__((aligned(1024))) char slot0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char slot1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char slot2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char slot3[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char slot4[kTileBytes];
+  char* const slots[kSlots] = {slot0, slot1, slot2, slot3, slot4};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -245,69 +263,92 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
   const int KT = g.K / kBK;
   da.kt_total = db.kt_total = KT;
   da.start = db.start = g.stagger > 0 ? (int)(((unsigned)grp * (unsigned)g.stagger) % (unsigned)KT) : 0;
-  // Prologue: slab 0 into stage 0.
-  da.issue(0, stage0, wave);
-  db.issue(0, stage0 + kTileBytes, wave);
-  wait_vmcnt<0>();
+  // Prologue: A_0 -> slot 0, B_0 -> slot 1, A_1 -> slot 2; wait for the
+  // first two (the A_1 requests, issued last, may still be in flight).
+  da.issue(0, slots[0], wave);
+  db.issue(0, slots[1], wave);
+  da.issue(KT > 1 ? 1 : 0, slots[2], wave);
+  wait_vmcnt<kDmaPerOp>();
   block_barrier();
 
   bf16x8 a0[4], b0[4], a1[4], b1[4];
-  fa.read(stage0, 0, a0);
-  fb.read(stage0 + kTileBytes, 0, b0);
+  fa.read(slots[0], 0, a0);
+  fb.read(slots[1], 0, b0);
 
   // LDS fragment reads per k step (ds_read_b128 per 32-row block, or two
   // ds_read_b64_tr_b16 for m-contiguous operands).
   constexpr int kReads = (A_KC ? 4 : 8) + (B_KC ? 4 : 8);
-  // One slab: multiply `slab` while the DMA refills `nxt` with slab kt + 1
-  // (`nxt` was last read in slab kt - 1, before the barrier that ended it).
-  // The last slab re-requests itself (L2 hits, never read) so the body
+  // One slab kt.  Ring: A_kt sits in slot 2kt mod 5 and B_kt in slot
+  // 2kt+1 mod 5.  During the slab, B_{kt+1} goes to slot 2kt+3 and A_{kt+2}
+  // to slot 2kt+4 (mod 5): the slots of A_{kt-1} and B_{kt-1}, whose last
+  // reads finished before the barrier that ended slab kt-1.  Requests past
+  // the last slab re-fetch the last slab (L2 hits, never read) so the body
   // stays one basic block.
-  auto slab_step = [&](int kt, char* slab, char* nxt) __attribute__((always_inline)) {
-    const int kn = kt + 1 < KT ? kt + 1 : kt;
-    fa.read(slab, 1, a1);
-    fb.read(slab + kTileBytes, 1, b1);
-    da.issue(kn, nxt, wave);
-    db.issue(kn, nxt + kTileBytes, wave);
+  auto slab_step = [&](int kt, char* sa, char* sb, char* sa1, char* sb1, char* sa2)
+      __attribute__((always_inline)) {
+    const int kn1 = kt + 1 < KT ? kt + 1 : KT - 1;
+    const int kn2 = kt + 2 < KT ? kt + 2 : KT - 1;
+    fa.read(sa, 1, a1);
+    fb.read(sb, 1, b1);
+    db.issue(kn1, sb1, wave);
+    da.issue(kn2, sa2, wave);
     mma<0, 4>(acc, a0, b0);
-    fa.read(slab, 2, a0);
-    fb.read(slab + kTileBytes, 2, b0);
+    fa.read(sa, 2, a0);
+    fb.read(sb, 2, b0);
     mma<0, 4>(acc, a1, b1);
-    fa.read(slab, 3, a1);
-    fb.read(slab + kTileBytes, 3, b1);
+    fa.read(sa, 3, a1);
+    fb.read(sb, 3, b1);
     mma<0, 4>(acc, a0, b0);
     mma<0, 2>(acc, a1, b1);
     // Issue order: each k step first requests all fragments of the next
-    // step, then runs its 16 MFMAs; the first step's MFMAs alternate with
-    // the 16 DMA requests of the next slab.
-    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+    // step, then runs its 16 MFMAs; the 16 DMA requests are spread over
+    // the first three steps (6, 5, 5), one per two or three MFMAs.
+    constexpr int kDma[3] = {6, 5, 5};
 #pragma unroll
-    for (int q = 0; q < 2 * kDmaPerOp; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    for (int s = 0; s < 3; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if ((q + 1) * kDma[s] / 16 > q * kDma[s] / 16)
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    // slab kt + 1 landed for every wave; every read of slab kt is done
+    // B_{kt+1} and everything before it landed (A_{kt+2}, the last
+    // kDmaPerOp requests, may not have); every read of slab kt is done.
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<0>();
+    wait_vmcnt<kDmaPerOp>();
     wait_lgkmcnt0();
     block_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    fa.read(nxt, 0, a0);
-    fb.read(nxt + kTileBytes, 0, b0);
+    fa.read(sa1, 0, a0);
+    fb.read(sb1, 0, b0);
     mma<2, 4>(acc, a1, b1);
     __builtin_amdgcn_sched_group_barrier(0x100, kReads, 1);
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
   };
+  // Slab kt with p = kt mod 5.
+  auto step = [&](int kt, int p) __attribute__((always_inline)) {
+    slab_step(kt, slots[(2 * p) % kSlots], slots[(2 * p + 1) % kSlots],
+              slots[(2 * p + 2) % kSlots], slots[(2 * p + 3) % kSlots],
+              slots[(2 * p + 4) % kSlots]);
+  };
   int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
-    slab_step(kt, stage0, stage1);
-    slab_step(kt + 1, stage1, stage0);
+  for (; kt + kSlots <= KT; kt += kSlots) {
+    step(kt, 0);
+    step(kt + 1, 1);
+    step(kt + 2, 2);
+    step(kt + 3, 3);
+    step(kt + 4, 4);
   }
-  if (kt < KT) slab_step(kt, stage0, stage1);
+  if (kt < KT) step(kt, 0);
+  if (kt + 1 < KT) step(kt + 1, 1);
+  if (kt + 2 < KT) step(kt + 2, 2);
+  if (kt + 3 < KT) step(kt + 3, 3);
+  // The last slab's look-ahead requests must land before the workgroup's
+  // LDS can be handed to another workgroup.
+  wait_vmcnt<0>();
 
   // Epilogue.  Accumulator r of lane l in block (i, j) is
   // D[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32] of that 32x32 block.
@@ -357,6 +398,9 @@ bool gemm_bf16_dma_supported(bool a_kc, bool b_kc, const GemmArgs& g) {
   if (g.K <= 0 || g.K % kBK != 0 || g.M <= 0 || g.N <= 0) return false;
   if (g.M % 8 != 0 || g.N % 8 != 0) return false;
   if ((g.lda % 8) || (g.ldb % 8) || (g.ldo % 4)) return false;
+  // Operand pieces are addressed by 32-bit offsets within 256 rows (k-
+  // contiguous) or 64 k-rows (m-contiguous) of a leading dimension.
+  if (g.lda >= (int64_t{1} << 22) || g.ldb >= (int64_t{1} << 22)) return false;
   const uintptr_t al = reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B) |
                        reinterpret_cast<uintptr_t>(g.out);
   if (al & 15u) return false;
