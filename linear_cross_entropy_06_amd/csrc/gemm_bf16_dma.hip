@@ -352,29 +352,73 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
 
   // Epilogue.  Accumulator r of lane l in block (i, j) is
   // D[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32] of that 32x32 block.
+  if constexpr (sizeof(OutT) == 2) {
+    // bf16 output (one launch of long K per tile: the epilogue is a small
+    // share of the tile's time): stored straight from the accumulators.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 128 + j * 32 + (lane & 31);
-      if (n >= g.N) continue;
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn * 128 + j * 32 + (lane & 31);
+        if (n >= g.N) continue;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = m0 + wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
-        if (m >= g.M) continue;  // M % 8 == 0: a run of 4 is all in or all out
-        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                         acc[i][j][4 * q + 3]};
-        const int64_t off = (int64_t)n * g.ldo + m;
-        if constexpr (EPI == kStoreOut && sizeof(OutT) == 2) {
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
+          if (m >= g.M) continue;  // M % 8 == 0: a run of 4 is all in or all out
           u32x2 w;
-          w[0] = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-          w[1] = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + off) = w;
-        } else {
-          float* o = static_cast<float*>(g.out) + off;
-          f32x4 w = v;
-          if (EPI == kAccumF32 && g.beta) w += *reinterpret_cast<const f32x4*>(o);
-          *reinterpret_cast<f32x4*>(o) = w;
+          w[0] = bf16_bits(acc[i][j][4 * q]) | (bf16_bits(acc[i][j][4 * q + 1]) << 16);
+          w[1] = bf16_bits(acc[i][j][4 * q + 2]) | (bf16_bits(acc[i][j][4 * q + 3]) << 16);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + (int64_t)n * g.ldo + m) = w;
+        }
+      }
+    }
+  } else {
+    // fp32 output: each lane holds 16-byte pieces of 32 different rows, so
+    // direct stores would send 32 partial-line requests per instruction.
+    // Each wave instead transposes one 32(m) x 128(n) block at a time
+    // through its own 16 KiB of LDS (chunk index XOR-swizzled by row pair,
+    // conflict-free on both sides) and reads it back with 8 lanes per
+    // 128-byte row segment: every store (and, when accumulating, every
+    // load of the previous value) covers 8 whole lines.
+    // All look-ahead DMA requests of every wave have landed once all waves
+    // pass this barrier; the operand ring is free.
+    block_barrier();
+    char* const buf = wave == 0 ? slot0 : wave == 1 ? slot1 : wave == 2 ? slot2 : slot3;
+    const bool accumulate = EPI == kAccumF32 && g.beta;
+    const int c_rd = lane & 7;  // 16-byte chunk this lane reads back
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      char* const b = buf + (i & 1) * 16384;
+      const int m = m0 + wm * 128 + i * 32 + 4 * c_rd;
+      f32x4 old[16];
+      if (accumulate) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int n = n0 + wn * 128 + 8 * t + (lane >> 3);
+          if (n < g.N && m < g.M)
+            old[t] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(g.out) +
+                                                     (int64_t)n * g.ldo + m);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int nl = 32 * j + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = 2 * q + (lane >> 5);
+          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                           acc[i][j][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(b + nl * 128 + ((c ^ ((nl >> 1) & 7)) << 4)) = v;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int nl = 8 * t + (lane >> 3);
+        f32x4 v = *reinterpret_cast<const f32x4*>(b + nl * 128 + ((c_rd ^ ((nl >> 1) & 7)) << 4));
+        const int n = n0 + wn * 128 + nl;
+        if (n < g.N && m < g.M) {
+          if (accumulate) v += old[t];
+          *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + (int64_t)n * g.ldo + m) = v;
         }
       }
     }
