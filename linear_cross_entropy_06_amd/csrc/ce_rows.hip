@@ -8,6 +8,9 @@
 //   pass 1  online maximum / sum of exponentials over the row, one wave64
 //           per row, lanes combined with cross-lane shuffles
 //           -> lse_i, row loss lse_i - z[i, t_i]
+//           (or, when the logits kernel left one log-sum-exp per 256-wide
+//           slice of the row, the same online reduction over those
+//           partials: the row is then read only once, by pass 2)
 //   pass 2  G[i, j] = (exp(z[i, j] - lse_i) - [j == t_i]) * scale, written
 //           back over the row itself (bf16 into the first half of the row's
 //           bytes, or fp32 in place).
@@ -84,11 +87,12 @@ __device__ __forceinline__ void combine(float& m, float& s, float m2, float s2) 
   m = mm;
 }
 
-template <bool VEC4, bool OUT_BF16>
+template <bool VEC4, bool OUT_BF16, bool PARTS>
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
 ce_rows_kernel(float* __restrict__ z, int64_t ldz, const int32_t* __restrict__ targets,
                int rows, int V, float scale, float* __restrict__ row_loss,
-               int64_t loss_stride) {
+               int64_t loss_stride, const float* __restrict__ row_part, int64_t ldp,
+               int n_part) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -100,7 +104,12 @@ ce_rows_kernel(float* __restrict__ z, int64_t ldz, const int32_t* __restrict__ t
   // ---- pass 1: online max / sum of exponentials (base 2) ----
   float m = -INFINITY, s = 0.0f;
   int j0 = 0;
-  if constexpr (VEC4) {
+  if constexpr (PARTS) {
+    // The logits kernel already reduced each 256-wide slice of the row to
+    // log2(sum 2^y); their log-sum-exp is the row's.
+    const float* pr = row_part + (int64_t)row * ldp;
+    for (int p = lane; p < n_part; p += 64) online_add(pr[p], m, s);
+  } else if constexpr (VEC4) {
     const int nvec = V >> 2;
     const f32x4* zv = reinterpret_cast<const f32x4*>(zr);
     int v = lane;
@@ -114,7 +123,8 @@ ce_rows_kernel(float* __restrict__ z, int64_t ldz, const int32_t* __restrict__ t
     for (; v < nvec; v += 64) online_add4(zv[v], m, s);
     j0 = nvec << 2;
   }
-  for (int j = j0 + lane; j < V; j += 64) online_add(to_log2(zr[j]), m, s);
+  if constexpr (!PARTS)
+    for (int j = j0 + lane; j < V; j += 64) online_add(to_log2(zr[j]), m, s);
 
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -206,24 +216,31 @@ loss_sum_kernel(const float* __restrict__ row_loss, int64_t loss_stride, int row
 
 hipError_t launch_ce_rows(float* z, int64_t ldz, const int32_t* targets, int rows,
                           int V, float scale, float* row_loss, int64_t loss_stride,
-                          bool out_bf16, hipStream_t s) {
+                          bool out_bf16, hipStream_t s, const float* row_part, int64_t ldp,
+                          int n_part) {
   if (rows <= 0) return hipSuccess;
   const dim3 grid((rows + kWavesPerBlock - 1) / kWavesPerBlock);
   const dim3 block(64 * kWavesPerBlock);
   // float4 path: row starts 16-byte aligned (base aligned, pitch % 4 == 0).
   const bool vec4 = ((ldz & 3) == 0) && ((reinterpret_cast<uintptr_t>(z) & 15) == 0);
-  if (vec4 && out_bf16)
-    hipLaunchKernelGGL((ce_rows_kernel<true, true>), grid, block, 0, s, z, ldz, targets,
-                       rows, V, scale, row_loss, loss_stride);
-  else if (vec4)
-    hipLaunchKernelGGL((ce_rows_kernel<true, false>), grid, block, 0, s, z, ldz, targets,
-                       rows, V, scale, row_loss, loss_stride);
-  else if (out_bf16)
-    hipLaunchKernelGGL((ce_rows_kernel<false, true>), grid, block, 0, s, z, ldz, targets,
-                       rows, V, scale, row_loss, loss_stride);
-  else
-    hipLaunchKernelGGL((ce_rows_kernel<false, false>), grid, block, 0, s, z, ldz, targets,
-                       rows, V, scale, row_loss, loss_stride);
+  if (row_part) {
+    // Partials come from the bf16 logits kernel, whose shapes give float4 rows.
+    if (!(vec4 && out_bf16) || n_part < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((ce_rows_kernel<true, true, true>), grid, block, 0, s, z, ldz, targets,
+                       rows, V, scale, row_loss, loss_stride, row_part, ldp, n_part);
+  } else if (vec4 && out_bf16) {
+    hipLaunchKernelGGL((ce_rows_kernel<true, true, false>), grid, block, 0, s, z, ldz, targets,
+                       rows, V, scale, row_loss, loss_stride, nullptr, 0, 0);
+  } else if (vec4) {
+    hipLaunchKernelGGL((ce_rows_kernel<true, false, false>), grid, block, 0, s, z, ldz,
+                       targets, rows, V, scale, row_loss, loss_stride, nullptr, 0, 0);
+  } else if (out_bf16) {
+    hipLaunchKernelGGL((ce_rows_kernel<false, true, false>), grid, block, 0, s, z, ldz,
+                       targets, rows, V, scale, row_loss, loss_stride, nullptr, 0, 0);
+  } else {
+    hipLaunchKernelGGL((ce_rows_kernel<false, false, false>), grid, block, 0, s, z, ldz,
+                       targets, rows, V, scale, row_loss, loss_stride, nullptr, 0, 0);
+  }
   return hipGetLastError();
 }
 

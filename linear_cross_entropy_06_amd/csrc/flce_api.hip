@@ -8,6 +8,8 @@
 //   1. logits   Z[C, V] (fp32, workspace)  = h_c W^T          MFMA
 //   2. rows     lse, row loss -> staged in grad_h's rows of the chunk;
 //               Z rewritten in place as G = (softmax - onehot) / N
+//               (lse from per-slice partials that step 1 staged there too,
+//               when its kernel provides them)
 //   3. loss     *loss (+)= sum(staged row losses) / N         fixed order
 //   4. grad_h   grad_h_c = G W      (overwrites the staged losses)
 //   5. grad_W   grad_W (+)= G^T h_c (written by the first chunk, then
@@ -95,6 +97,7 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
   const int64_t ldg = bf16 ? 2 * V : V;
   float* z = static_cast<float*>(workspace);
   const int64_t loss_stride = H * es / 4;  // floats between staged row losses
+  const int64_t n_part = (V + flce::kRowPartTile - 1) / flce::kRowPartTile;
 
   for (int64_t r0 = 0; r0 < N; r0 += C) {
     const int rows = static_cast<int>((N - r0) < C ? (N - r0) : C);
@@ -103,10 +106,19 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
     float* staged = reinterpret_cast<float*>(ghc);
     hipError_t e;
 
-    // 1. Z^T = W . h_c^T, stored as Z[i][j] (row pitch V floats).
+    // 1. Z^T = W . h_c^T, stored as Z[i][j] (row pitch V floats).  When the
+    //    direct-to-LDS kernel runs it also leaves one log-sum-exp per
+    //    256-wide slice of each row in the chunk's grad_h rows, after the
+    //    staged loss (so step 2 reads Z once).
     flce::GemmArgs g1{W, H, hc, H, z, V, static_cast<int>(V), rows, static_cast<int>(H), 0};
     g1.group_m = 4;
     g1.stagger = 37;
+    const bool parts = bf16 && 1 + n_part <= loss_stride &&
+                       flce::gemm_bf16_uses_dma(true, true, vec, g1);
+    if (parts) {
+      g1.row_part = staged + 1;
+      g1.ldp = loss_stride;
+    }
     mk.before();
     e = gemm(dt, true, true, flce::kStoreF32, vec, g1, stream);
     mk.after();
@@ -115,7 +127,8 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
     // 2. lse and row losses; Z -> G in place.
     mk.before();
     e = flce::launch_ce_rows(z, V, targets + r0, rows, static_cast<int>(V), inv_n, staged,
-                             loss_stride, bf16, stream);
+                             loss_stride, bf16, stream, parts ? staged + 1 : nullptr,
+                             loss_stride, static_cast<int>(n_part));
     mk.after();
     if (e != hipSuccess) return FLCE_ERR_HIP;
 

@@ -76,6 +76,21 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return u >> 16;
 }
 
+// z * log2(e) rounded once (never fused into a following operation), the
+// same rounding the row cross-entropy kernel applies to the stored logits.
+__device__ __forceinline__ float to_log2(float z) {
+#pragma clang fp contract(off)
+  return z * 1.4426950408889634f;
+}
+
+// (m, s) <- (max, sum of 2^(y - max)) of the union of two partial sums.
+__device__ __forceinline__ void lse2_combine(float& m, float& s, float m2, float s2) {
+  const float mm = fmaxf(m, m2);
+  if (mm == -__builtin_inff()) return;  // both empty
+  s = s * __builtin_amdgcn_exp2f(m - mm) + s2 * __builtin_amdgcn_exp2f(m2 - mm);
+  m = mm;
+}
+
 // s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt left open).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -386,6 +401,10 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
     char* const buf = wave == 0 ? slot0 : wave == 1 ? slot1 : wave == 2 ? slot2 : slot3;
     const bool accumulate = EPI == kAccumF32 && g.beta;
     const int c_rd = lane & 7;  // 16-byte chunk this lane reads back
+    // Running base-2 (max, sum) per column j for the row log-sum-exp
+    // partials (GemmArgs::row_part).
+    float pm[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       char* const b = buf + (i & 1) * 16384;
@@ -411,6 +430,31 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
           *reinterpret_cast<f32x4*>(b + nl * 128 + ((c ^ ((nl >> 1) & 7)) << 4)) = v;
         }
       }
+      if (EPI == kStoreF32 && g.row_part != nullptr) {
+        // Fold block i into the running base-2 (max, sum) of each column.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float y[16];
+          float bm = -__builtin_inff();
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bool ok = m0 + wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5) < g.M;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              y[4 * q + e] = ok ? to_log2(acc[i][j][4 * q + e]) : -__builtin_inff();
+              bm = fmaxf(bm, y[4 * q + e]);
+            }
+          }
+          if (bm > pm[j]) {
+            ps[j] *= __builtin_amdgcn_exp2f(pm[j] - bm);
+            pm[j] = bm;
+          }
+          if (pm[j] != -__builtin_inff()) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ps[j] += __builtin_amdgcn_exp2f(y[r] - pm[j]);
+          }
+        }
+      }
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         const int nl = 8 * t + (lane >> 3);
@@ -419,6 +463,39 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
         if (n < g.N && m < g.M) {
           if (accumulate) v += old[t];
           *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + (int64_t)n * g.ldo + m) = v;
+        }
+      }
+    }
+    if (EPI == kStoreF32 && g.row_part != nullptr) {
+      // Base-2 log-sum-exp of this tile's column slice for every n: each
+      // lane has folded its 64 values of column n = 32 j + l % 32 (rows
+      // m >= M excluded) into (pm[j], ps[j]) block by block above; pair
+      // with lane l ^ 32 (the other half of the 32-row blocks), then the
+      // wave holding the other 128 rows of the tile hands its (max, sum)
+      // over through LDS.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float m2 = __shfl_xor(pm[j], 32, 64);
+        const float s2 = __shfl_xor(ps[j], 32, 64);
+        lse2_combine(pm[j], ps[j], m2, s2);
+      }
+      float* const xch = reinterpret_cast<float*>(slot4) + wn * 256;
+      if (wm == 1 && lane < 32) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xch[2 * (32 * j + lane)] = pm[j];
+          xch[2 * (32 * j + lane) + 1] = ps[j];
+        }
+      }
+      wait_lgkmcnt0();  // the hand-over is in LDS before the barrier
+      block_barrier();  // (no fence: the output stores need not drain)
+      if (wm == 0 && lane < 32) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lse2_combine(pm[j], ps[j], xch[2 * (32 * j + lane)], xch[2 * (32 * j + lane) + 1]);
+          const int n = n0 + wn * 128 + 32 * j + lane;
+          // Every tile holds at least 8 rows m < M, so the sum is >= 1.
+          if (n < g.N) g.row_part[(int64_t)n * g.ldp + tmi] = pm[j] + __builtin_amdgcn_logf(ps[j]);
         }
       }
     }

@@ -124,6 +124,12 @@ TINY = [
     (300, 136, 520, 100, "bf16"),
     (300, 136, 523, 256, "bf16"),
     (513, 264, 1000, 257, "bf16"),
+    # H % 64 == 0: the logits run on the direct-to-LDS kernel, which also
+    # leaves the per-256-column log-sum-exp partials the row pass consumes
+    (300, 128, 1000, 128, "bf16"),   # ragged last vocabulary tile (232 rows)
+    (520, 192, 2056, 256, "bf16"),   # last vocabulary tile holds 8 rows
+    (512, 256, 768, 256, "bf16"),    # all three contractions on that kernel
+    (64, 64, 40000, 64, "bf16"),     # partials exceed a grad_h row: two-pass rows
     (3, 8, 5, 2, "f32"),
     (17, 24, 1000, 7, "f32"),
     (100, 64, 333, 33, "f32"),
