@@ -148,7 +148,9 @@ ce_rows_kernel(float* __restrict__ z, int64_t ldz, const int32_t* __restrict__ t
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int v = v0 + lane + 64 * u;
-        if (v < nvec) x[u] = zv[v];
+        // Streaming: the row is read once here and its G is consumed by
+        // the next GEMM long after other rows have gone through the caches.
+        if (v < nvec) x[u] = __builtin_nontemporal_load(&zv[v]);
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -164,7 +166,7 @@ ce_rows_kernel(float* __restrict__ z, int64_t ldz, const int32_t* __restrict__ t
           u32x2 w;
           w[0] = bf16_bits(g[0]) | (bf16_bits(g[1]) << 16);
           w[1] = bf16_bits(g[2]) | (bf16_bits(g[3]) << 16);
-          reinterpret_cast<u32x2*>(gb)[v] = w;
+          __builtin_nontemporal_store(w, &reinterpret_cast<u32x2*>(gb)[v]);
         } else {
           zv[v] = g;
         }

@@ -315,18 +315,27 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
     fb.read(sb, 3, b1);
     mma<0, 4>(acc, a0, b0);
     mma<0, 2>(acc, a1, b1);
-    // Issue order: each k step first requests all fragments of the next
-    // step, then runs its 16 MFMAs; the 16 DMA requests are spread over
-    // the first three steps (6, 5, 5), one per two or three MFMAs.
+    // Issue order: each k step requests the fragments of the next step
+    // while its 16 MFMAs run, and the 16 DMA requests are spread over the
+    // first three steps (6, 5, 5), one per two or three MFMAs.  With an
+    // m-contiguous A (two transposing reads per fragment) half the reads
+    // go up front and the rest one per MFMA over the first eight (fewer
+    // cycles per slab, measured); the k/k kernel issues all eight first.
     constexpr int kDma[3] = {6, 5, 5};
+    constexpr int kPre = A_KC ? kReads : kReads / 2;
+    constexpr int kSpread = kReads - kPre;
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if ((q + 1) * kDma[s] / 16 > q * kDma[s] / 16)
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (kSpread && q < 8) {
+          const int nr = (q + 1) * kSpread / 8 - q * kSpread / 8;
+          for (int r = 0; r < nr; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
