@@ -40,6 +40,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kWavesPerBlock = 4;
 constexpr int kUnroll = 4;  // float4 loads in flight per lane
 
+// Two floats rounded to nearest-even bf16 and packed (first in the low
+// half): one v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
@@ -140,6 +148,44 @@ ce_rows_kernel(float* __restrict__ z, int64_t ldz, const int32_t* __restrict__ t
 
   // ---- pass 2: rewrite the row as (softmax - onehot) * scale ----
   uint16_t* gb = reinterpret_cast<uint16_t*>(zr);
+  if constexpr (PARTS) {
+    // (bf16 output, V % 8 == 0.)  Every element becomes
+    // 2^(z log2 e - lse2 + log2 scale): one fma and one exp per logit; the
+    // target's element is then rewritten as (p_t - 1) * scale.
+    const float shift = lse2 - log2_hw(scale);
+    const int nvec = V >> 2;
+    const f32x4* zv = reinterpret_cast<const f32x4*>(zr);
+    for (int v0 = 0; v0 < nvec; v0 += 64 * kUnroll) {
+      f32x4 x[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int v = v0 + lane + 64 * u;
+        // Streaming: the row is read once here and its G is consumed by
+        // the next GEMM long after other rows have gone through the caches.
+        if (v < nvec) x[u] = __builtin_nontemporal_load(&zv[v]);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int v = v0 + lane + 64 * u;
+        if (v >= nvec) continue;
+        float g[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) g[e] = exp2_hw(__builtin_fmaf(x[u][e], kLog2e, -shift));
+        u32x2 w;
+        w[0] = pack_bf16x2(g[0], g[1]);
+        w[1] = pack_bf16x2(g[2], g[3]);
+        __builtin_nontemporal_store(w, &reinterpret_cast<u32x2*>(gb)[v]);
+      }
+    }
+    if (t_ok && lane == 0) {
+      // After this wave's stores of the row have completed (the target's
+      // element among them), overwrite that element.
+      __builtin_amdgcn_s_waitcnt(0);
+      const float pt = exp2_hw(to_log2(zt) - lse2);
+      gb[t] = (uint16_t)bf16_bits((pt - 1.0f) * scale);
+    }
+    return;
+  }
   if constexpr (VEC4) {
     const int nvec = V >> 2;
     f32x4* zv = reinterpret_cast<f32x4*>(zr);
@@ -164,8 +210,8 @@ ce_rows_kernel(float* __restrict__ z, int64_t ldz, const int32_t* __restrict__ t
         }
         if constexpr (OUT_BF16) {
           u32x2 w;
-          w[0] = bf16_bits(g[0]) | (bf16_bits(g[1]) << 16);
-          w[1] = bf16_bits(g[2]) | (bf16_bits(g[3]) << 16);
+          w[0] = pack_bf16x2(g[0], g[1]);
+          w[1] = pack_bf16x2(g[2], g[3]);
           __builtin_nontemporal_store(w, &reinterpret_cast<u32x2*>(gb)[v]);
         } else {
           zv[v] = g;

@@ -69,11 +69,12 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return (b % kXcds) * per + b / kXcds;
 }
 
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two floats rounded to nearest-even bf16 and packed (first in the low
+// half): one v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // z * log2(e) rounded once (never fused into a following operation), the
@@ -390,8 +391,8 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
           const int m = m0 + wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
           if (m >= g.M) continue;  // M % 8 == 0: a run of 4 is all in or all out
           u32x2 w;
-          w[0] = bf16_bits(acc[i][j][4 * q]) | (bf16_bits(acc[i][j][4 * q + 1]) << 16);
-          w[1] = bf16_bits(acc[i][j][4 * q + 2]) | (bf16_bits(acc[i][j][4 * q + 3]) << 16);
+          w[0] = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+          w[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
           *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + (int64_t)n * g.ldo + m) = w;
         }
       }
