@@ -1,27 +1,35 @@
 // Row kernels of the fused linear + cross-entropy head (gfx950).
 //
-// ce_rows: per token row of fp32 logits (page 3, "Complete Guide to Liger
-// Kernel", section "LigerCrossEntropyLoss": cross entropy of the logits
-// against the labels; page 1, "Liger Kernel explained", section "What does
-// Liger Kernel actually fuse": the gradient comes out of the same pass and
-// is recomputed from the logits instead of being stored separately):
-//   pass 1  online maximum / sum of exponentials over the row, one wave64
-//           per row, lanes combined with cross-lane shuffles
-//           -> lse_i, row loss lse_i - z[i, t_i]
-//           (or, when the logits kernel left one log-sum-exp per 256-wide
-//           slice of the row, the same online reduction over those
-//           partials: the row is then read only once, by pass 2)
+// Per token row (page 3, "Complete Guide to Liger Kernel", section
+// "LigerCrossEntropyLoss": cross entropy of the logits against the labels;
+// page 1, "Liger Kernel explained", section "What does Liger Kernel actually
+// fuse": the gradient comes out of the same pass and is recomputed from the
+// logits instead of being stored separately), one wave64 per row:
+//
+// ce_rows (from fp32 logits)
+//   pass 1  online maximum / sum of exponentials over the row, lanes
+//           combined with cross-lane shuffles -> lse_i, row loss
+//           lse_i - z[i, t_i]
 //   pass 2  G[i, j] = (exp(z[i, j] - lse_i) - [j == t_i]) * scale, written
 //           back over the row itself (bf16 into the first half of the row's
 //           bytes, or fp32 in place).
-// The exponentials run in base 2 on the hardware v_exp_f32 / v_log_f32.
+//   In-place safety: a wave reads a slab of its row into registers and only
+//   then writes the slab's results, whose bytes (2 per element, starting at
+//   the row's first byte) lie at or below bytes the wave has already read
+//   (4 per element); within one wave, memory operations are issued in
+//   program order and every store depends on the loads it follows.
 //
-// In-place safety: a wave owns its row, reads a slab of the row into
-// registers and only then writes the slab's results, whose bytes (2 per
-// element, starting at the row's first byte) lie at or below bytes the wave
-// has already read (4 per element).  Within one wave, memory operations are
-// issued in program order and every store depends on the loads it follows,
-// so no barrier is needed.
+// ce_rows_exp (from the logits kernel's exponentiated output: bf16
+// u = 2^(y - mx_q) with y = z log2 e, and one (mx_q, s_q = sum of u) pair
+// per 128-column half tile q of the row)
+//   lse2_i  = log2 sum_q s_q 2^(mx_q), by the same online reduction over the
+//             pairs
+//   z[i, t] = h_i . W_t, recomputed (bf16 rows, fp32 accumulation)
+//   G[i, j] = u * 2^(mx_q - lse2_i) * scale, written over u element by
+//             element (same place, same size), then G[i, t] is rewritten as
+//             (2^(z[i,t] log2 e - lse2_i) - 1) * scale.
+//
+// The exponentials run in base 2 on the hardware v_exp_f32 / v_log_f32.
 //
 // loss_sum: the per-row losses of a chunk, summed in fp64 in a fixed order
 // (deterministic), scaled and added to the running fp32 loss.
@@ -95,12 +103,11 @@ __device__ __forceinline__ void combine(float& m, float& s, float m2, float s2) 
   m = mm;
 }
 
-template <bool VEC4, bool OUT_BF16, bool PARTS>
+template <bool VEC4, bool OUT_BF16>
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
 ce_rows_kernel(float* __restrict__ z, int64_t ldz, const int32_t* __restrict__ targets,
                int rows, int V, float scale, float* __restrict__ row_loss,
-               int64_t loss_stride, const float* __restrict__ row_part, int64_t ldp,
-               int n_part) {
+               int64_t loss_stride) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -112,12 +119,7 @@ ce_rows_kernel(float* __restrict__ z, int64_t ldz, const int32_t* __restrict__ t
   // ---- pass 1: online max / sum of exponentials (base 2) ----
   float m = -INFINITY, s = 0.0f;
   int j0 = 0;
-  if constexpr (PARTS) {
-    // The logits kernel already reduced each 256-wide slice of the row to
-    // log2(sum 2^y); their log-sum-exp is the row's.
-    const float* pr = row_part + (int64_t)row * ldp;
-    for (int p = lane; p < n_part; p += 64) online_add(pr[p], m, s);
-  } else if constexpr (VEC4) {
+  if constexpr (VEC4) {
     const int nvec = V >> 2;
     const f32x4* zv = reinterpret_cast<const f32x4*>(zr);
     int v = lane;
@@ -131,8 +133,7 @@ ce_rows_kernel(float* __restrict__ z, int64_t ldz, const int32_t* __restrict__ t
     for (; v < nvec; v += 64) online_add4(zv[v], m, s);
     j0 = nvec << 2;
   }
-  if constexpr (!PARTS)
-    for (int j = j0 + lane; j < V; j += 64) online_add(to_log2(zr[j]), m, s);
+  for (int j = j0 + lane; j < V; j += 64) online_add(to_log2(zr[j]), m, s);
 
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -148,44 +149,6 @@ ce_rows_kernel(float* __restrict__ z, int64_t ldz, const int32_t* __restrict__ t
 
   // ---- pass 2: rewrite the row as (softmax - onehot) * scale ----
   uint16_t* gb = reinterpret_cast<uint16_t*>(zr);
-  if constexpr (PARTS) {
-    // (bf16 output, V % 8 == 0.)  Every element becomes
-    // 2^(z log2 e - lse2 + log2 scale): one fma and one exp per logit; the
-    // target's element is then rewritten as (p_t - 1) * scale.
-    const float shift = lse2 - log2_hw(scale);
-    const int nvec = V >> 2;
-    const f32x4* zv = reinterpret_cast<const f32x4*>(zr);
-    for (int v0 = 0; v0 < nvec; v0 += 64 * kUnroll) {
-      f32x4 x[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int v = v0 + lane + 64 * u;
-        // Streaming: the row is read once here and its G is consumed by
-        // the next GEMM long after other rows have gone through the caches.
-        if (v < nvec) x[u] = __builtin_nontemporal_load(&zv[v]);
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int v = v0 + lane + 64 * u;
-        if (v >= nvec) continue;
-        float g[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) g[e] = exp2_hw(__builtin_fmaf(x[u][e], kLog2e, -shift));
-        u32x2 w;
-        w[0] = pack_bf16x2(g[0], g[1]);
-        w[1] = pack_bf16x2(g[2], g[3]);
-        __builtin_nontemporal_store(w, &reinterpret_cast<u32x2*>(gb)[v]);
-      }
-    }
-    if (t_ok && lane == 0) {
-      // After this wave's stores of the row have completed (the target's
-      // element among them), overwrite that element.
-      __builtin_amdgcn_s_waitcnt(0);
-      const float pt = exp2_hw(to_log2(zt) - lse2);
-      gb[t] = (uint16_t)bf16_bits((pt - 1.0f) * scale);
-    }
-    return;
-  }
   if constexpr (VEC4) {
     const int nvec = V >> 2;
     f32x4* zv = reinterpret_cast<f32x4*>(zr);
@@ -239,6 +202,93 @@ ce_rows_kernel(float* __restrict__ z, int64_t ldz, const int32_t* __restrict__ t
   }
 }
 
+// bf16 -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int UNROLL>
+__global__ void __launch_bounds__(64 * kWavesPerBlock)
+ce_rows_exp_kernel(uint16_t* __restrict__ u, int64_t ldu, const float* __restrict__ row_part,
+                   int64_t ldp, const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+                   int H, const int32_t* __restrict__ targets, int rows, int V, float scale,
+                   float* __restrict__ row_loss, int64_t loss_stride) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int t = targets[row];
+  const bool t_ok = (t >= 0) && (t < V);
+
+  // lse2 from the (max, sum) pairs of the row's half tiles.
+  const float* pr = row_part + (int64_t)row * ldp;
+  const int nq = (V + kHalfTile - 1) / kHalfTile;
+  float m = -INFINITY, s = 0.0f;
+  for (int q = lane; q < nq; q += 64) combine(m, s, pr[2 * q], pr[2 * q + 1]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off, 64);
+    const float s2 = __shfl_xor(s, off, 64);
+    combine(m, s, m2, s2);
+  }
+  const float lse2 = m + log2_hw(s);
+
+  // Target logit z_t = h_row . W_t (an out-of-range target is never
+  // dereferenced: the loss becomes NaN).
+  float zt = __builtin_nanf("");
+  if (t_ok) {
+    const u32x4* hv = reinterpret_cast<const u32x4*>(h + (int64_t)row * H);
+    const u32x4* wv = reinterpret_cast<const u32x4*>(W + (int64_t)t * H);
+    float acc = 0.0f;
+    for (int k = lane; k < H / 8; k += 64) {
+      const u32x4 a = hv[k], b = wv[k];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc += bf16_lo(a[e]) * bf16_lo(b[e]) + bf16_hi(a[e]) * bf16_hi(b[e]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    zt = acc;
+  }
+  if (lane == 0) row_loss[(int64_t)row * loss_stride] = (lse2 - to_log2(zt)) * kLn2;
+
+  // G = u * 2^(mx_q - lse2) * scale, in place, 8 elements (one half-tile
+  // slice) per lane and step.
+  const float shift = lse2 - log2_hw(scale);
+  uint16_t* ur = u + (int64_t)row * ldu;
+  u32x4* uv = reinterpret_cast<u32x4*>(ur);
+  const int nvec = V >> 3;
+  for (int v0 = 0; v0 < nvec; v0 += 64 * UNROLL) {
+    u32x4 x[UNROLL];
+    float f[UNROLL];
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {
+      const int v = v0 + lane + 64 * k;
+      if (v < nvec) {
+        x[k] = __builtin_nontemporal_load(&uv[v]);
+        f[k] = pr[2 * (v >> 4)];  // mx of the half tile holding elements 8v .. 8v+7
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {
+      const int v = v0 + lane + 64 * k;
+      if (v >= nvec) continue;
+      const float c = exp2_hw(f[k] - shift);
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(bf16_lo(x[k][e]) * c, bf16_hi(x[k][e]) * c);
+      __builtin_nontemporal_store(w, &uv[v]);
+    }
+  }
+  if (t_ok && lane == 0) {
+    // After this wave's stores of the row have completed (the target's
+    // element among them), overwrite that element.
+    __builtin_amdgcn_s_waitcnt(0);
+    const float pt = exp2_hw(to_log2(zt) - lse2);
+    ur[t] = (uint16_t)bf16_bits((pt - 1.0f) * scale);
+  }
+}
+
 constexpr int kSumThreads = 256;
 
 __global__ void __launch_bounds__(kSumThreads)
@@ -264,31 +314,41 @@ loss_sum_kernel(const float* __restrict__ row_loss, int64_t loss_stride, int row
 
 hipError_t launch_ce_rows(float* z, int64_t ldz, const int32_t* targets, int rows,
                           int V, float scale, float* row_loss, int64_t loss_stride,
-                          bool out_bf16, hipStream_t s, const float* row_part, int64_t ldp,
-                          int n_part) {
+                          bool out_bf16, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const dim3 grid((rows + kWavesPerBlock - 1) / kWavesPerBlock);
   const dim3 block(64 * kWavesPerBlock);
   // float4 path: row starts 16-byte aligned (base aligned, pitch % 4 == 0).
   const bool vec4 = ((ldz & 3) == 0) && ((reinterpret_cast<uintptr_t>(z) & 15) == 0);
-  if (row_part) {
-    // Partials come from the bf16 logits kernel, whose shapes give float4 rows.
-    if (!(vec4 && out_bf16) || n_part < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((ce_rows_kernel<true, true, true>), grid, block, 0, s, z, ldz, targets,
-                       rows, V, scale, row_loss, loss_stride, row_part, ldp, n_part);
-  } else if (vec4 && out_bf16) {
-    hipLaunchKernelGGL((ce_rows_kernel<true, true, false>), grid, block, 0, s, z, ldz, targets,
-                       rows, V, scale, row_loss, loss_stride, nullptr, 0, 0);
-  } else if (vec4) {
-    hipLaunchKernelGGL((ce_rows_kernel<true, false, false>), grid, block, 0, s, z, ldz,
-                       targets, rows, V, scale, row_loss, loss_stride, nullptr, 0, 0);
-  } else if (out_bf16) {
-    hipLaunchKernelGGL((ce_rows_kernel<false, true, false>), grid, block, 0, s, z, ldz,
-                       targets, rows, V, scale, row_loss, loss_stride, nullptr, 0, 0);
-  } else {
-    hipLaunchKernelGGL((ce_rows_kernel<false, false, false>), grid, block, 0, s, z, ldz,
-                       targets, rows, V, scale, row_loss, loss_stride, nullptr, 0, 0);
-  }
+  if (vec4 && out_bf16)
+    hipLaunchKernelGGL((ce_rows_kernel<true, true>), grid, block, 0, s, z, ldz, targets,
+                       rows, V, scale, row_loss, loss_stride);
+  else if (vec4)
+    hipLaunchKernelGGL((ce_rows_kernel<true, false>), grid, block, 0, s, z, ldz, targets,
+                       rows, V, scale, row_loss, loss_stride);
+  else if (out_bf16)
+    hipLaunchKernelGGL((ce_rows_kernel<false, true>), grid, block, 0, s, z, ldz, targets,
+                       rows, V, scale, row_loss, loss_stride);
+  else
+    hipLaunchKernelGGL((ce_rows_kernel<false, false>), grid, block, 0, s, z, ldz, targets,
+                       rows, V, scale, row_loss, loss_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_rows_exp(uint16_t* u, int64_t ldu, const float* row_part, int64_t ldp,
+                              const uint16_t* h, const uint16_t* W, int H,
+                              const int32_t* targets, int rows, int V, float scale,
+                              float* row_loss, int64_t loss_stride, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  // 16-byte pieces of u, h and W rows; one (max, sum) pair per half tile.
+  if ((V % 8) || (ldu % 8) || (H % 8) || (reinterpret_cast<uintptr_t>(u) & 15) ||
+      (reinterpret_cast<uintptr_t>(h) & 15) || (reinterpret_cast<uintptr_t>(W) & 15) ||
+      ldp < 2 * ((V + kHalfTile - 1) / kHalfTile))
+    return hipErrorInvalidValue;
+  const dim3 grid((rows + kWavesPerBlock - 1) / kWavesPerBlock);
+  const dim3 block(64 * kWavesPerBlock);
+  hipLaunchKernelGGL((ce_rows_exp_kernel<4>), grid, block, 0, s, u, ldu, row_part, ldp, h, W, H,
+                     targets, rows, V, scale, row_loss, loss_stride);
   return hipGetLastError();
 }
 

@@ -5,11 +5,14 @@
 // Per token chunk of C rows (page 1, "Liger Kernel explained", section
 // "What does Liger Kernel actually fuse": only a chunk of logits is ever
 // resident, and its gradient is formed before the next chunk):
-//   1. logits   Z[C, V] (fp32, workspace)  = h_c W^T          MFMA
+//   1. logits   Z[C, V] = h_c W^T (workspace)                 MFMA
+//               bf16 inputs on the direct-to-LDS kernel: stored as
+//               u = 2^(Z log2 e - mx) in bf16 with one (mx, sum u) pair per
+//               128-column half tile, so the row pass reads 2 bytes per
+//               logit and the workspace is chunk * V * 2 bytes plus the
+//               pairs; otherwise fp32 Z
 //   2. rows     lse, row loss -> staged in grad_h's rows of the chunk;
-//               Z rewritten in place as G = (softmax - onehot) / N
-//               (lse from per-slice partials that step 1 staged there too,
-//               when its kernel provides them)
+//               the logits rewritten in place as G = (softmax - onehot) / N
 //   3. loss     *loss (+)= sum(staged row losses) / N         fixed order
 //   4. grad_h   grad_h_c = G W      (overwrites the staged losses)
 //   5. grad_W   grad_W (+)= G^T h_c (written by the first chunk, then
@@ -37,13 +40,26 @@ inline hipError_t gemm(flce_dtype dt, bool a_kc, bool b_kc, int epi, bool vec,
                          : flce::launch_gemm_f32(a_kc, b_kc, epi, g, s);
 }
 
+// The bf16 path whose logits kernel writes exponentiated bf16 logits and
+// their (max, sum) pairs (direct-to-LDS kernel: K = H a multiple of 64,
+// V a multiple of 8).  Every other case keeps fp32 logits.
+inline bool exp_path(int64_t H, int64_t V, flce_dtype dt) {
+  return dt == FLCE_BF16 && V % 8 == 0 && H % 64 == 0 && H < (int64_t{1} << 22) &&
+         flce::gemm_bf16_dma_enabled();
+}
+
+// (max, sum) pairs per row on the exponentiated path.
+inline int64_t n_half_tiles(int64_t V) { return (V + flce::kHalfTile - 1) / flce::kHalfTile; }
+
 }  // namespace
 
 extern "C" size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk,
                                        flce_dtype dt) {
   if (!dims_ok(N) || !dims_ok(H) || !dims_ok(V) || chunk < 1 || !dtype_ok(dt)) return 0;
-  const int64_t C = chunk < N ? chunk : N;
-  return static_cast<size_t>(C) * static_cast<size_t>(V) * 4u;
+  const size_t C = static_cast<size_t>(chunk < N ? chunk : N);
+  if (exp_path(H, V, dt))  // bf16 logits of one chunk + 2 floats per row and half tile
+    return C * static_cast<size_t>(V) * 2u + C * static_cast<size_t>(n_half_tiles(V)) * 8u;
+  return C * static_cast<size_t>(V) * 4u;  // fp32 logits of one chunk
 }
 
 extern "C" int64_t flce_launch_count(int64_t N, int64_t chunk) {
@@ -91,13 +107,19 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
   const int64_t es = esize(dt);
   const bool bf16 = dt == FLCE_BF16;
   const bool vec = (V % 8) == 0;
+  const bool expo = exp_path(H, V, dt);
   const float inv_n = static_cast<float>(1.0 / static_cast<double>(N));
-  // G's row pitch in its own elements: bf16 G lives in the first half of
-  // each fp32 logit row, fp32 G replaces the row.
-  const int64_t ldg = bf16 ? 2 * V : V;
+  // Workspace: fp32 logits Z (row pitch V) that become G in place (bf16 G in
+  // the first half of each row, fp32 G over the row), or on the
+  // exponentiated path bf16 u (row pitch V) that becomes bf16 G in place,
+  // followed by the rows' (max, sum) pairs.
+  const int64_t ldg = expo ? V : (bf16 ? 2 * V : V);
   float* z = static_cast<float*>(workspace);
+  uint16_t* u = static_cast<uint16_t*>(workspace);
+  const int64_t ldp = 2 * n_half_tiles(V);
+  float* pairs = reinterpret_cast<float*>(static_cast<char*>(workspace) + C * V * 2);
+  void* g_base = workspace;
   const int64_t loss_stride = H * es / 4;  // floats between staged row losses
-  const int64_t n_part = (V + flce::kRowPartTile - 1) / flce::kRowPartTile;
 
   for (int64_t r0 = 0; r0 < N; r0 += C) {
     const int rows = static_cast<int>((N - r0) < C ? (N - r0) : C);
@@ -106,29 +128,32 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
     float* staged = reinterpret_cast<float*>(ghc);
     hipError_t e;
 
-    // 1. Z^T = W . h_c^T, stored as Z[i][j] (row pitch V floats).  When the
-    //    direct-to-LDS kernel runs it also leaves one log-sum-exp per
-    //    256-wide slice of each row in the chunk's grad_h rows, after the
-    //    staged loss (so step 2 reads Z once).
-    flce::GemmArgs g1{W, H, hc, H, z, V, static_cast<int>(V), rows, static_cast<int>(H), 0};
+    // 1. Z^T = W . h_c^T, stored as Z[i][j] (row pitch V), or as its
+    //    exponentiated bf16 form with (max, sum) pairs.
+    flce::GemmArgs g1{W, H, hc, H, workspace, V, static_cast<int>(V), rows, static_cast<int>(H),
+                      0};
     g1.group_m = 4;
     g1.stagger = 37;
-    const bool parts = bf16 && 1 + n_part <= loss_stride &&
-                       flce::gemm_bf16_uses_dma(true, true, vec, g1);
-    if (parts) {
-      g1.row_part = staged + 1;
-      g1.ldp = loss_stride;
+    if (expo) {
+      g1.row_part = pairs;
+      g1.ldp = ldp;
     }
     mk.before();
-    e = gemm(dt, true, true, flce::kStoreF32, vec, g1, stream);
+    e = expo ? flce::launch_gemm_bf16(true, true, flce::kExpBF16, vec, g1, stream)
+             : gemm(dt, true, true, flce::kStoreF32, vec, g1, stream);
     mk.after();
     if (e != hipSuccess) return FLCE_ERR_HIP;
 
-    // 2. lse and row losses; Z -> G in place.
+    // 2. lse and row losses (staged in the chunk's grad_h rows); the logits
+    //    become G in place.
     mk.before();
-    e = flce::launch_ce_rows(z, V, targets + r0, rows, static_cast<int>(V), inv_n, staged,
-                             loss_stride, bf16, stream, parts ? staged + 1 : nullptr,
-                             loss_stride, static_cast<int>(n_part));
+    e = expo ? flce::launch_ce_rows_exp(u, V, pairs, ldp, static_cast<const uint16_t*>(
+                                            static_cast<const void*>(hc)),
+                                        static_cast<const uint16_t*>(W), static_cast<int>(H),
+                                        targets + r0, rows, static_cast<int>(V), inv_n, staged,
+                                        loss_stride, stream)
+             : flce::launch_ce_rows(z, V, targets + r0, rows, static_cast<int>(V), inv_n,
+                                    staged, loss_stride, bf16, stream);
     mk.after();
     if (e != hipSuccess) return FLCE_ERR_HIP;
 
@@ -140,7 +165,8 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
 
     // 4. grad_h_c^T = W^T . G^T: A(m = hidden, k = vocab) = W[k][m],
     //    B(n = token, k = vocab) = G[n][k].
-    flce::GemmArgs g4{W, H, z, ldg, ghc, H, static_cast<int>(H), rows, static_cast<int>(V), 0};
+    flce::GemmArgs g4{W, H, g_base, ldg, ghc, H, static_cast<int>(H), rows, static_cast<int>(V),
+                      0};
     g4.group_m = 4;
     mk.before();
     e = gemm(dt, false, true, flce::kStoreOut, vec, g4, stream);
@@ -149,8 +175,8 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
 
     // 5. grad_W^T (+)= h_c^T . G: A(m = hidden, k = token) = h_c[k][m],
     //    B(n = vocab, k = token) = G[k][n].
-    flce::GemmArgs g5{hc, H, z, ldg, grad_W, H, static_cast<int>(H), static_cast<int>(V), rows,
-                      r0 == 0 ? 0 : 1};
+    flce::GemmArgs g5{hc, H, g_base, ldg, grad_W, H, static_cast<int>(H), static_cast<int>(V),
+                      rows, r0 == 0 ? 0 : 1};
     g5.group_m = 4;
     g5.stagger = 37;
     mk.before();

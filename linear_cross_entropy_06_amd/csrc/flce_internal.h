@@ -17,7 +17,16 @@ enum Epilogue : int {
   kStoreF32 = 0,   // out (fp32) = D
   kStoreOut = 1,   // out (operand dtype: bf16 or fp32) = D
   kAccumF32 = 2,   // out (fp32) = D + (beta ? out : 0)
+  // Exponentiated logits (direct-to-LDS kernel, k/k operands only): with
+  // y = D * log2(e) and, per output column n and 128-row half tile q of m,
+  // mx = max of y over the half tile's rows m < M:
+  //   out (bf16) = 2^(y - mx)
+  //   row_part[n * ldp + 2q] = mx,  row_part[n * ldp + 2q + 1] = sum of 2^(y - mx)
+  kExpBF16 = 3,
 };
+
+// Rows of m per (max, sum) pair of the kExpBF16 epilogue.
+constexpr int kHalfTile = 128;
 
 struct GemmArgs {
   const void* A;
@@ -34,16 +43,10 @@ struct GemmArgs {
   // K-start rotation per tile group: group g starts its K walk at slab
   // (g * stagger) mod (K / 64); 0 disables it.
   int stagger = 0;
-  // Optional (kStoreF32 through the direct-to-LDS kernel only): for every
-  // output column n and every 256-row tile t of m, row_part[n * ldp + t] =
-  // log2(sum over the tile's rows m < M of 2^(D[m][n] * log2 e)), the
-  // tile's share of a row log-sum-exp, with D[m][n] * log2 e rounded once.
+  // (max, sum) pairs of the kExpBF16 epilogue; ldp in floats.
   float* row_part = nullptr;
   int64_t ldp = 0;
 };
-
-// Rows of m per tile of the direct-to-LDS kernel (granularity of row_part).
-constexpr int kRowPartTile = 256;
 
 // bf16 operands, MFMA 32x32x16, fp32 accumulation.  `vec` selects the
 // 16-byte load/store path, valid when every dimension that is contiguous in
@@ -56,8 +59,11 @@ hipError_t launch_gemm_bf16(bool a_kc, bool b_kc, int epi, bool vec,
 // gemm_bf16_dma.hip; valid when gemm_bf16_dma_supported() holds.
 bool gemm_bf16_dma_supported(bool a_kc, bool b_kc, const GemmArgs& g);
 // True when launch_gemm_bf16 with these arguments runs the direct-to-LDS
-// kernel (the only one that fills GemmArgs::row_part).
+// kernel (the only one with the kExpBF16 epilogue).
 bool gemm_bf16_uses_dma(bool a_kc, bool b_kc, bool vec, const GemmArgs& g);
+// Whether the direct-to-LDS kernel may be used at all in this process (it
+// can be switched off for comparisons, see gemm_bf16.hip).
+bool gemm_bf16_dma_enabled();
 hipError_t launch_gemm_bf16_dma(bool a_kc, bool b_kc, int epi, const GemmArgs& g,
                                 hipStream_t s);
 
@@ -66,15 +72,19 @@ hipError_t launch_gemm_f32(bool a_kc, bool b_kc, int epi, const GemmArgs& g,
                            hipStream_t s);
 
 // Cross entropy of `rows` fp32 logit rows with the gradient rewritten in
-// place (bf16 at pitch 2*ldz elements, or fp32 at pitch ldz).  With
-// row_part != nullptr the row log-sum-exp is assembled from the n_part
-// per-tile partials row_part[row * ldp + t] (GemmArgs::row_part) and each
-// row is read once; otherwise it is read twice (online max / sum first).
+// place (bf16 at pitch 2*ldz elements, or fp32 at pitch ldz).
 hipError_t launch_ce_rows(float* z, int64_t ldz, const int32_t* targets,
                           int rows, int V, float scale, float* row_loss,
-                          int64_t loss_stride, bool out_bf16, hipStream_t s,
-                          const float* row_part = nullptr, int64_t ldp = 0,
-                          int n_part = 0);
+                          int64_t loss_stride, bool out_bf16, hipStream_t s);
+
+// The same from exponentiated logits (kExpBF16 output u at pitch ldu, with
+// its (max, sum) pairs): u is rewritten in place as the bf16 gradient.  The
+// target logit of row i is recomputed as the dot product of h[i] and
+// W[targets[i]] (bf16 rows of H elements, fp32 accumulation).
+hipError_t launch_ce_rows_exp(uint16_t* u, int64_t ldu, const float* row_part, int64_t ldp,
+                              const uint16_t* h, const uint16_t* W, int H,
+                              const int32_t* targets, int rows, int V, float scale,
+                              float* row_loss, int64_t loss_stride, hipStream_t s);
 
 // loss[0] = (first ? 0 : loss[0]) + (sum of rows staged losses) * scale,
 // summed in fp64 in a fixed order.

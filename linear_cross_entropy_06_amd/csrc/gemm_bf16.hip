@@ -353,6 +353,8 @@ bool dma_enabled() {
 
 }  // namespace
 
+bool gemm_bf16_dma_enabled() { return dma_enabled(); }
+
 bool gemm_bf16_uses_dma(bool a_kc, bool b_kc, bool vec, const GemmArgs& g) {
   return vec && dma_enabled() && gemm_bf16_dma_supported(a_kc, b_kc, g);
 }
@@ -364,8 +366,8 @@ hipError_t launch_gemm_bf16(bool a_kc, bool b_kc, int epi, bool vec,
   // the larger operand stays in L2 across consecutive tiles.
   const int m_fastest = g.M < g.N ? 1 : 0;
   if (gemm_bf16_uses_dma(a_kc, b_kc, vec, g)) return launch_gemm_bf16_dma(a_kc, b_kc, epi, g, s);
-  // Row log-sum-exp partials are produced by the direct-to-LDS kernel only.
-  if (g.row_part) return hipErrorInvalidValue;
+  // Exponentiated logits are produced by the direct-to-LDS kernel only.
+  if (epi == kExpBF16) return hipErrorInvalidValue;
   if (a_kc && b_kc && epi == kStoreF32)       // logits
     return launch_layout<true, true, kStoreF32, float>(vec, g, m_fastest, s);
   if (!a_kc && b_kc && epi == kStoreOut)      // grad_h (bf16 out)

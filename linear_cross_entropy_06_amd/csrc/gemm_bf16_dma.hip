@@ -77,19 +77,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-// z * log2(e) rounded once (never fused into a following operation), the
-// same rounding the row cross-entropy kernel applies to the stored logits.
+// z * log2(e) rounded once (never fused into a following operation).
 __device__ __forceinline__ float to_log2(float z) {
 #pragma clang fp contract(off)
   return z * 1.4426950408889634f;
-}
-
-// (m, s) <- (max, sum of 2^(y - max)) of the union of two partial sums.
-__device__ __forceinline__ void lse2_combine(float& m, float& s, float m2, float s2) {
-  const float mm = fmaxf(m, m2);
-  if (mm == -__builtin_inff()) return;  // both empty
-  s = s * __builtin_amdgcn_exp2f(m - mm) + s2 * __builtin_amdgcn_exp2f(m2 - mm);
-  m = mm;
 }
 
 // s_waitcnt with only vmcnt constrained (expcnt / lgkmcnt left open).
@@ -377,7 +368,7 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
 
   // Epilogue.  Accumulator r of lane l in block (i, j) is
   // D[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32] of that 32x32 block.
-  if constexpr (sizeof(OutT) == 2) {
+  if constexpr (EPI == kStoreOut && sizeof(OutT) == 2) {
     // bf16 output (one launch of long K per tile: the epilogue is a small
     // share of the tile's time): stored straight from the accumulators.
 #pragma unroll
@@ -398,114 +389,125 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
       }
     }
   } else {
-    // fp32 output: each lane holds 16-byte pieces of 32 different rows, so
-    // direct stores would send 32 partial-line requests per instruction.
-    // Each wave instead transposes one 32(m) x 128(n) block at a time
-    // through its own 16 KiB of LDS (chunk index XOR-swizzled by row pair,
-    // conflict-free on both sides) and reads it back with 8 lanes per
-    // 128-byte row segment: every store (and, when accumulating, every
-    // load of the previous value) covers 8 whole lines.
+    // Each lane holds 16-byte pieces of 32 different output rows, so direct
+    // stores would send 32 partial-line requests per instruction.  Each wave
+    // instead transposes its results a block at a time through its own
+    // 16 KiB of LDS, laid out [128 n][128 bytes of m] with the 16-byte chunk
+    // index XOR-swizzled by row pair (conflict-free both ways), and reads it
+    // back with 8 lanes per 128-byte row segment: every store (and, when
+    // accumulating, every load of the previous value) covers whole lines.
     // All look-ahead DMA requests of every wave have landed once all waves
     // pass this barrier; the operand ring is free.
     block_barrier();
     char* const buf = wave == 0 ? slot0 : wave == 1 ? slot1 : wave == 2 ? slot2 : slot3;
-    const bool accumulate = EPI == kAccumF32 && g.beta;
     const int c_rd = lane & 7;  // 16-byte chunk this lane reads back
-    // Running base-2 (max, sum) per column j for the row log-sum-exp
-    // partials (GemmArgs::row_part).
-    float pm[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      char* const b = buf + (i & 1) * 16384;
-      const int m = m0 + wm * 128 + i * 32 + 4 * c_rd;
-      f32x4 old[16];
-      if (accumulate) {
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int n = n0 + wn * 128 + 8 * t + (lane >> 3);
-          if (n < g.N && m < g.M)
-            old[t] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(g.out) +
-                                                     (int64_t)n * g.ldo + m);
-        }
-      }
+    auto lds_off = [](int nl, int c) { return nl * 128 + ((c ^ ((nl >> 1) & 7)) << 4); };
+    if constexpr (EPI == kExpBF16) {
+      // Exponentiated logits in bf16 (32(m) x 128(n) blocks i = 2p, 2p+1
+      // fill one 128-byte row segment of m), and per column and half tile
+      // the (max, sum) pair.  Lanes l and l ^ 32 hold the two halves of
+      // every 32-row block, so one shuffle completes a column over the
+      // wave's 128 rows.
+      constexpr float kL2e = 1.4426950408889634f;
+      const int hl = lane >> 5;
+      float mneg[4], ssum[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int nl = 32 * j + (lane & 31);
+        float mz = -__builtin_inff();
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = 2 * q + (lane >> 5);
-          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                           acc[i][j][4 * q + 3]};
-          *reinterpret_cast<f32x4*>(b + nl * 128 + ((c ^ ((nl >> 1) & 7)) << 4)) = v;
-        }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (m0 + wm * 128 + i * 32 + 8 * q + 4 * hl < g.M)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) mz = fmaxf(mz, acc[i][j][4 * q + e]);
+        mz = fmaxf(mz, __shfl_xor(mz, 32, 64));
+        // No row of this half tile below M: nothing is stored for it.
+        mneg[j] = mz == -__builtin_inff() ? 0.0f : -to_log2(mz);
+        ssum[j] = 0.0f;
       }
-      if (EPI == kStoreF32 && g.row_part != nullptr) {
-        // Fold block i into the running base-2 (max, sum) of each column.
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float y[16];
-          float bm = -__builtin_inff();
+      for (int p = 0; p < 2; ++p) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bool ok = m0 + wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5) < g.M;
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * p + ii;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              y[4 * q + e] = ok ? to_log2(acc[i][j][4 * q + e]) : -__builtin_inff();
-              bm = fmaxf(bm, y[4 * q + e]);
+          for (int j = 0; j < 4; ++j) {
+            const int nl = 32 * j + (lane & 31);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const bool ok = m0 + wm * 128 + i * 32 + 8 * q + 4 * hl < g.M;
+              float u[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                u[e] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * q + e], kL2e,
+                                                                   mneg[j]))
+                          : 0.0f;
+              ssum[j] += (u[0] + u[1]) + (u[2] + u[3]);
+              const u32x2 w = {pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3])};
+              *reinterpret_cast<u32x2*>(buf + lds_off(nl, 4 * ii + q) + 8 * hl) = w;
             }
           }
-          if (bm > pm[j]) {
-            ps[j] *= __builtin_amdgcn_exp2f(pm[j] - bm);
-            pm[j] = bm;
-          }
-          if (pm[j] != -__builtin_inff()) {
+        }
+        const int m = m0 + wm * 128 + 64 * p + 8 * c_rd;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) ps[j] += __builtin_amdgcn_exp2f(y[r] - pm[j]);
-          }
+        for (int t = 0; t < 16; ++t) {
+          const int nl = 8 * t + (lane >> 3);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(buf + lds_off(nl, c_rd));
+          const int n = n0 + wn * 128 + nl;
+          if (n < g.N && m < g.M)  // M % 8 == 0: a run of 8 is all in or all out
+            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.out) + (int64_t)n * g.ldo + m) = v;
         }
       }
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int nl = 8 * t + (lane >> 3);
-        f32x4 v = *reinterpret_cast<const f32x4*>(b + nl * 128 + ((c_rd ^ ((nl >> 1) & 7)) << 4));
-        const int n = n0 + wn * 128 + nl;
-        if (n < g.N && m < g.M) {
-          if (accumulate) v += old[t];
-          *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + (int64_t)n * g.ldo + m) = v;
-        }
-      }
-    }
-    if (EPI == kStoreF32 && g.row_part != nullptr) {
-      // Base-2 log-sum-exp of this tile's column slice for every n: each
-      // lane has folded its 64 values of column n = 32 j + l % 32 (rows
-      // m >= M excluded) into (pm[j], ps[j]) block by block above; pair
-      // with lane l ^ 32 (the other half of the 32-row blocks), then the
-      // wave holding the other 128 rows of the tile hands its (max, sum)
-      // over through LDS.
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float m2 = __shfl_xor(pm[j], 32, 64);
-        const float s2 = __shfl_xor(ps[j], 32, 64);
-        lse2_combine(pm[j], ps[j], m2, s2);
-      }
-      float* const xch = reinterpret_cast<float*>(slot4) + wn * 256;
-      if (wm == 1 && lane < 32) {
+      for (int j = 0; j < 4; ++j) ssum[j] += __shfl_xor(ssum[j], 32, 64);
+      if (lane < 32 && m0 + wm * 128 < g.M) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          xch[2 * (32 * j + lane)] = pm[j];
-          xch[2 * (32 * j + lane) + 1] = ps[j];
-        }
-      }
-      wait_lgkmcnt0();  // the hand-over is in LDS before the barrier
-      block_barrier();  // (no fence: the output stores need not drain)
-      if (wm == 0 && lane < 32) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          lse2_combine(pm[j], ps[j], xch[2 * (32 * j + lane)], xch[2 * (32 * j + lane) + 1]);
           const int n = n0 + wn * 128 + 32 * j + lane;
-          // Every tile holds at least 8 rows m < M, so the sum is >= 1.
-          if (n < g.N) g.row_part[(int64_t)n * g.ldp + tmi] = pm[j] + __builtin_amdgcn_logf(ps[j]);
+          if (n < g.N) {
+            float* pr = g.row_part + (int64_t)n * g.ldp + 2 * (2 * tmi + wm);
+            pr[0] = -mneg[j];
+            pr[1] = ssum[j];
+          }
+        }
+      }
+    } else {
+      // fp32 output: one 32(m) x 128(n) block i at a time, double-buffered.
+      const bool accumulate = EPI == kAccumF32 && g.beta;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        char* const b = buf + (i & 1) * 16384;
+        const int m = m0 + wm * 128 + i * 32 + 4 * c_rd;
+        f32x4 old[16];
+        if (accumulate) {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const int n = n0 + wn * 128 + 8 * t + (lane >> 3);
+            if (n < g.N && m < g.M)
+              old[t] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(g.out) +
+                                                       (int64_t)n * g.ldo + m);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int nl = 32 * j + (lane & 31);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                             acc[i][j][4 * q + 3]};
+            *reinterpret_cast<f32x4*>(b + lds_off(nl, 2 * q + (lane >> 5))) = v;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int nl = 8 * t + (lane >> 3);
+          f32x4 v = *reinterpret_cast<const f32x4*>(b + lds_off(nl, c_rd));
+          const int n = n0 + wn * 128 + nl;
+          if (n < g.N && m < g.M) {
+            if (accumulate) v += old[t];
+            *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + (int64_t)n * g.ldo + m) = v;
+          }
         }
       }
     }
@@ -527,7 +529,9 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
 
 bool gemm_bf16_dma_supported(bool a_kc, bool b_kc, const GemmArgs& g) {
   if (g.K <= 0 || g.K % kBK != 0 || g.M <= 0 || g.N <= 0) return false;
-  if (g.M % 8 != 0 || g.N % 8 != 0) return false;
+  // m runs of 8 (stores, m-contiguous A chunks); n runs of 8 only when B
+  // is n-contiguous.
+  if (g.M % 8 != 0 || (!b_kc && g.N % 8 != 0)) return false;
   if ((g.lda % 8) || (g.ldb % 8) || (g.ldo % 4)) return false;
   // Operand pieces are addressed by 32-bit offsets within 256 rows (k-
   // contiguous) or 64 k-rows (m-contiguous) of a leading dimension.
@@ -536,13 +540,18 @@ bool gemm_bf16_dma_supported(bool a_kc, bool b_kc, const GemmArgs& g) {
                        reinterpret_cast<uintptr_t>(g.out);
   if (al & 15u) return false;
   (void)a_kc;
-  (void)b_kc;
   return true;
 }
 
 hipError_t launch_gemm_bf16_dma(bool a_kc, bool b_kc, int epi, const GemmArgs& g,
                                 hipStream_t s) {
   if (a_kc && b_kc && epi == kStoreF32) return launch_dma<true, true, kStoreF32, float>(g, s);
+  if (a_kc && b_kc && epi == kExpBF16) {
+    // 16-byte bf16 row pieces, (max, sum) pairs for every half tile
+    if ((g.ldo % 8) || !g.row_part || g.ldp < 2 * ((g.M + kHalfTile - 1) / kHalfTile))
+      return hipErrorInvalidValue;
+    return launch_dma<true, true, kExpBF16, uint16_t>(g, s);
+  }
   if (!a_kc && b_kc && epi == kStoreOut)
     return launch_dma<false, true, kStoreOut, uint16_t>(g, s);
   if (!a_kc && !b_kc && epi == kAccumF32)

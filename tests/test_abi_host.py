@@ -51,9 +51,16 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_workspace_bytes(lib):
     f = lib.flce_workspace_bytes
-    assert f(8192, 4096, 128256, 4096, BF16) == 4096 * 128256 * 4
-    assert f(8192, 4096, 128256, 2048, BF16) == 2048 * 128256 * 4
+    # bf16 with H % 64 == 0 and V % 8 == 0: exponentiated bf16 logits of one
+    # chunk plus two floats per row and 128-column half tile
+    assert f(8192, 4096, 128256, 4096, BF16) == 4096 * 128256 * 2 + 4096 * 1002 * 8
+    assert f(8192, 4096, 128256, 2048, BF16) == 2048 * 128256 * 2 + 2048 * 1002 * 8
+    assert f(8192, 3584, 256000, 4096, BF16) == 4096 * 256000 * 2 + 4096 * 2000 * 8
+    assert f(300, 128, 1000, 128, BF16) == 128 * 1000 * 2 + 128 * 8 * 8
+    # otherwise fp32 logits of one chunk
     assert f(100, 8, 5, 1000, BF16) == 100 * 5 * 4          # chunk clamped to N
+    assert f(300, 136, 1000, 100, BF16) == 100 * 1000 * 4     # H % 64 != 0
+    assert f(300, 128, 1001, 100, BF16) == 100 * 1001 * 4     # V % 8 != 0
     assert f(256, 128, 1000, 256, F32) == 256 * 1000 * 4
     # never above the fp32 logits of one chunk, always below the naive N*V*4
     for (N, V, C) in [(16384, 128256, 2048), (8192, 256000, 4096)]:
