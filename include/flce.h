@@ -60,9 +60,17 @@ typedef enum flce_status {
 } flce_status;
 
 /*
- * Bytes of device workspace flce_fwd_bwd needs: min(chunk, N) * V * 4, the
- * fp32 logits of one token chunk (the logits of all N tokens would take
- * N * V * 4).  Returns 0 when a size is < 1.  Pure host function.
+ * Bytes of device workspace flce_fwd_bwd needs, with C = min(chunk, N):
+ *   bf16 inputs, H % 64 == 0, V % 8 == 0:
+ *        C * V * 2 + C * ceil(V / 128) * 8   (the logits of one token chunk
+ *        kept as bf16 exponentials, plus two floats per row and 128-column
+ *        slice)
+ *   otherwise:
+ *        C * V * 4                           (the fp32 logits of one chunk)
+ * (FLCE_GEMM_GENERIC=1 in the environment, which switches the direct-to-LDS
+ * GEMM off for comparisons, selects the second form.)
+ * Either is at most C * V * 4; the logits of all N tokens would take
+ * N * V * 4.  Returns 0 when a size is < 1.  Pure host function.
  */
 size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk,
                             flce_dtype dt);
