@@ -100,6 +100,35 @@ flce_status flce_fwd_bwd(const void* h, const void* W, const int32_t* targets,
                          flce_dtype dt, hipStream_t stream);
 
 /*
+ * flce_fwd_bwd for gradient accumulation over micro-batches (page 3,
+ * "Complete Guide to Liger Kernel", the training-loop example: the loss of
+ * each micro-batch is backpropagated and the optimizer steps every few
+ * micro-batches): identical, except that grad_W is ADDED to, i.e. on
+ * return grad_W = (its previous contents) + dloss/dW, accumulated in fp32
+ * from the first token chunk on.  loss and grad_h are overwritten as in
+ * flce_fwd_bwd.  grad_W must hold initialised values.
+ */
+flce_status flce_fwd_bwd_accumulate(const void* h, const void* W, const int32_t* targets,
+                                    int64_t N, int64_t H, int64_t V, int64_t chunk,
+                                    float* loss, void* grad_h, float* grad_W,
+                                    void* workspace, size_t workspace_bytes,
+                                    flce_dtype dt, hipStream_t stream);
+
+/*
+ * Multiplies precomputed gradients in place by the upstream gradient of
+ * the loss, for a backward pass whose loss was scaled after the fused call
+ * (page 3's training loop divides it by the accumulation steps):
+ *   grad_h[0 .. n_h) *= *scale   (dt; bf16 rounded to nearest even)
+ *   grad_W[0 .. n_W) *= *scale   (fp32)
+ * scale is a DEVICE pointer to one fp32 value, read by the kernel, so the
+ * host never synchronises to learn it.  A buffer with n = 0 may be null;
+ * non-null buffers must be 16-byte aligned (FLCE_ERR_UNSUPPORTED),
+ * negative counts or a null scale give FLCE_ERR_INVALID_ARG.
+ */
+flce_status flce_scale_grads(void* grad_h, int64_t n_h, float* grad_W, int64_t n_W,
+                             const float* scale, flce_dtype dt, hipStream_t stream);
+
+/*
  * Kernel launches flce_fwd_bwd makes for these sizes: FLCE_STEPS per token
  * chunk, i.e. FLCE_STEPS * ceil(N / min(chunk, N)).  0 if a size is < 1.
  */

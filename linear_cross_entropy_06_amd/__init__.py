@@ -12,12 +12,15 @@ from ._lib import (
     FlceError,
     HipEvents,
     LIB_PATH,
+    LinearCrossEntropyFunction,
     STEP_NAMES,
     ce_rows,
     fwd_bwd,
     launch_count,
+    linear_cross_entropy,
     load,
     logits,
+    scale_grads,
     workspace_bytes,
 )
 
@@ -29,11 +32,14 @@ __all__ = [
     "FlceError",
     "HipEvents",
     "LIB_PATH",
+    "LinearCrossEntropyFunction",
     "STEP_NAMES",
     "ce_rows",
     "fwd_bwd",
     "launch_count",
+    "linear_cross_entropy",
     "load",
     "logits",
+    "scale_grads",
     "workspace_bytes",
 ]

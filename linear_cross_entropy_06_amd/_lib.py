@@ -33,6 +33,8 @@ STATUS = {
 EXPORTS = (
     "flce_workspace_bytes",
     "flce_fwd_bwd",
+    "flce_fwd_bwd_accumulate",
+    "flce_scale_grads",
     "flce_launch_count",
     "flce_fwd_bwd_timed",
     "flce_logits",
@@ -68,6 +70,10 @@ def load() -> ctypes.CDLL:
     lib.flce_fwd_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, sz,
                                  ctypes.c_int, vp]
     lib.flce_fwd_bwd.restype = ctypes.c_int
+    lib.flce_fwd_bwd_accumulate.argtypes = lib.flce_fwd_bwd.argtypes
+    lib.flce_fwd_bwd_accumulate.restype = ctypes.c_int
+    lib.flce_scale_grads.argtypes = [vp, i64, vp, i64, vp, ctypes.c_int, vp]
+    lib.flce_scale_grads.restype = ctypes.c_int
     lib.flce_launch_count.argtypes = [i64, i64]
     lib.flce_launch_count.restype = i64
     lib.flce_fwd_bwd_timed.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, sz,
@@ -160,11 +166,14 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
             grad_W: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None,
             events: Optional[HipEvents] = None,
+            accumulate: bool = False,
             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Mean cross-entropy loss of h W^T against targets, with dloss/dh and
     dloss/dW, via ``flce_fwd_bwd`` (or ``flce_fwd_bwd_timed`` when
-    ``events`` is given).  Returns (loss [] fp32, grad_h like h, grad_W
-    [V, H] fp32).  Buffers may be passed in to avoid allocation."""
+    ``events`` is given, or ``flce_fwd_bwd_accumulate`` when ``accumulate``:
+    dloss/dW is then added to the given fp32 ``grad_W``).  Returns (loss []
+    fp32, grad_h like h, grad_W [V, H] fp32).  Buffers may be passed in to
+    avoid allocation."""
     lib = load()
     _need_cuda(h, W, targets)
     if targets.dtype != torch.int32:
@@ -181,7 +190,11 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
     if grad_h is None:
         grad_h = torch.empty_like(h)
     if grad_W is None:
+        if accumulate:
+            raise ValueError("accumulate=True adds into a given grad_W")
         grad_W = torch.empty((V, H), dtype=torch.float32, device=dev)
+    if accumulate and events is not None:
+        raise ValueError("the timed entry point does not accumulate")
     need = int(lib.flce_workspace_bytes(N, H, V, chunk, dt))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
@@ -190,7 +203,9 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
             loss.data_ptr(), grad_h.data_ptr(), grad_W.data_ptr(),
             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
             dt, _stream_ptr(dev))
-    if events is None:
+    if accumulate:
+        st = lib.flce_fwd_bwd_accumulate(*args)
+    elif events is None:
         st = lib.flce_fwd_bwd(*args)
     else:
         st = lib.flce_fwd_bwd_timed(*args, events.array, events.n)
@@ -229,3 +244,56 @@ def ce_rows(z: torch.Tensor, targets: torch.Tensor, scale: float, out_dtype: tor
                             float(scale), row_loss.data_ptr(), 1, dt,
                             _stream_ptr(z.device)))
     return row_loss
+
+
+def scale_grads(grad_h: Optional[torch.Tensor], grad_W: Optional[torch.Tensor],
+                scale: torch.Tensor) -> None:
+    """grad_h *= scale and grad_W *= scale in place (``flce_scale_grads``);
+    ``scale`` is a one-element fp32 tensor on the GPU, read by the kernel."""
+    lib = load()
+    _need_cuda(scale)
+    if scale.dtype != torch.float32 or scale.numel() != 1:
+        raise TypeError("scale must be a one-element float32 tensor")
+    dev = scale.device
+    dt = FLCE_BF16
+    ph, nh, pw, nw = None, 0, None, 0
+    if grad_h is not None:
+        _need_cuda(grad_h)
+        dt = _dt(grad_h)
+        ph, nh = grad_h.data_ptr(), grad_h.numel()
+    if grad_W is not None:
+        _need_cuda(grad_W)
+        if grad_W.dtype != torch.float32:
+            raise TypeError("grad_W must be float32")
+        pw, nw = grad_W.data_ptr(), grad_W.numel()
+    _check(lib.flce_scale_grads(ph, nh, pw, nw, scale.data_ptr(), dt, _stream_ptr(dev)))
+
+
+class LinearCrossEntropyFunction(torch.autograd.Function):
+    """Autograd node for the fused head: the forward call computes the mean
+    loss and both gradients at once; backward only scales them by the
+    incoming gradient of the loss (on the GPU, without a host sync).  The
+    returned gradient of W is fp32; autograd casts it to W's dtype when it
+    accumulates into W.grad.  One backward per forward (the stored
+    gradients are scaled in place)."""
+
+    @staticmethod
+    def forward(ctx, h, W, targets, chunk):
+        loss, grad_h, grad_W = fwd_bwd(h.detach(), W.detach(), targets, chunk)
+        ctx.save_for_backward(grad_h, grad_W)
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        grad_h, grad_W = ctx.saved_tensors
+        need_h, need_W = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        scale = grad_out.detach().to(torch.float32).reshape(1).contiguous()
+        scale_grads(grad_h if need_h else None, grad_W if need_W else None, scale)
+        return (grad_h if need_h else None, grad_W if need_W else None, None, None)
+
+
+def linear_cross_entropy(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                         chunk: Optional[int] = None) -> torch.Tensor:
+    """Mean cross entropy of h W^T against int32 targets as a differentiable
+    op (the logits are never materialised)."""
+    return LinearCrossEntropyFunction.apply(h, W, targets, chunk)

@@ -88,7 +88,7 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
                          int64_t H, int64_t V, int64_t chunk, float* loss, void* grad_h,
                          float* grad_W, void* workspace, size_t workspace_bytes,
                          flce_dtype dt, hipStream_t stream, hipEvent_t* events,
-                         int64_t n_events) {
+                         int64_t n_events, bool accumulate) {
   if (!h || !W || !targets || !loss || !grad_h || !grad_W || !workspace)
     return FLCE_ERR_INVALID_ARG;
   if (!dims_ok(N) || !dims_ok(H) || !dims_ok(V) || chunk < 1 || !dtype_ok(dt))
@@ -176,7 +176,7 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
     // 5. grad_W^T (+)= h_c^T . G: A(m = hidden, k = token) = h_c[k][m],
     //    B(n = vocab, k = token) = G[k][n].
     flce::GemmArgs g5{hc, H, g_base, ldg, grad_W, H, static_cast<int>(H), static_cast<int>(V),
-                      rows, r0 == 0 ? 0 : 1};
+                      rows, (r0 == 0 && !accumulate) ? 0 : 1};
     g5.group_m = 4;
     g5.stagger = 37;
     mk.before();
@@ -195,7 +195,31 @@ extern "C" flce_status flce_fwd_bwd(const void* h, const void* W, const int32_t*
                                     void* workspace, size_t workspace_bytes, flce_dtype dt,
                                     hipStream_t stream) {
   return fwd_bwd_impl(h, W, targets, N, H, V, chunk, loss, grad_h, grad_W, workspace,
-                      workspace_bytes, dt, stream, nullptr, 0);
+                      workspace_bytes, dt, stream, nullptr, 0, false);
+}
+
+extern "C" flce_status flce_fwd_bwd_accumulate(const void* h, const void* W,
+                                               const int32_t* targets, int64_t N, int64_t H,
+                                               int64_t V, int64_t chunk, float* loss,
+                                               void* grad_h, float* grad_W, void* workspace,
+                                               size_t workspace_bytes, flce_dtype dt,
+                                               hipStream_t stream) {
+  return fwd_bwd_impl(h, W, targets, N, H, V, chunk, loss, grad_h, grad_W, workspace,
+                      workspace_bytes, dt, stream, nullptr, 0, true);
+}
+
+extern "C" flce_status flce_scale_grads(void* grad_h, int64_t n_h, float* grad_W, int64_t n_W,
+                                        const float* scale, flce_dtype dt,
+                                        hipStream_t stream) {
+  if (!scale || n_h < 0 || n_W < 0 || !dtype_ok(dt)) return FLCE_ERR_INVALID_ARG;
+  if ((n_h > 0 && !grad_h) || (n_W > 0 && !grad_W)) return FLCE_ERR_INVALID_ARG;
+  if ((n_h > 0 && !aligned16(grad_h)) || (n_W > 0 && !aligned16(grad_W)) ||
+      (reinterpret_cast<uintptr_t>(scale) & 3u))
+    return FLCE_ERR_UNSUPPORTED;
+  if (flce::launch_scale(grad_h, n_h, dt == FLCE_BF16, scale, stream) != hipSuccess ||
+      flce::launch_scale(grad_W, n_W, false, scale, stream) != hipSuccess)
+    return FLCE_ERR_HIP;
+  return FLCE_OK;
 }
 
 extern "C" flce_status flce_fwd_bwd_timed(const void* h, const void* W,
@@ -207,7 +231,7 @@ extern "C" flce_status flce_fwd_bwd_timed(const void* h, const void* W,
                                           int64_t n_events) {
   if (!events) return FLCE_ERR_INVALID_ARG;
   return fwd_bwd_impl(h, W, targets, N, H, V, chunk, loss, grad_h, grad_W, workspace,
-                      workspace_bytes, dt, stream, events, n_events);
+                      workspace_bytes, dt, stream, events, n_events, false);
 }
 
 extern "C" flce_status flce_logits(const void* h, const void* W, int64_t rows, int64_t H,

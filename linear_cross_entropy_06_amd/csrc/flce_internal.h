@@ -86,6 +86,10 @@ hipError_t launch_ce_rows_exp(uint16_t* u, int64_t ldu, const float* row_part, i
                               const int32_t* targets, int rows, int V, float scale,
                               float* row_loss, int64_t loss_stride, hipStream_t s);
 
+// x[0 .. n) *= *s in place (bf16 with round to nearest even, or fp32); x
+// 16-byte aligned, s a device pointer.
+hipError_t launch_scale(void* x, int64_t n, bool bf16, const float* s, hipStream_t st);
+
 // loss[0] = (first ? 0 : loss[0]) + (sum of rows staged losses) * scale,
 // summed in fp64 in a fixed order.
 hipError_t launch_loss_sum(const float* row_loss, int64_t loss_stride,

@@ -38,6 +38,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     assert names == sorted(["flce_workspace_bytes", "flce_fwd_bwd", "flce_launch_count",
                             "flce_fwd_bwd_timed", "flce_logits", "flce_ce_rows",
+                            "flce_fwd_bwd_accumulate", "flce_scale_grads",
                             "flce_status_string"])
 
 
@@ -73,34 +74,53 @@ def test_workspace_bytes(lib):
 P = 4096  # a 16-byte aligned stand-in address; never dereferenced below
 
 
-def _call(lib, **kw):
+ENTRY = ["flce_fwd_bwd", "flce_fwd_bwd_accumulate"]
+
+
+def _call(lib, entry="flce_fwd_bwd", **kw):
     a = dict(h=P, W=P, t=P, N=4, H=8, V=5, chunk=2, loss=P, gh=P, gW=P, ws=P,
              wsb=1 << 20, dt=BF16, stream=None)
     a.update(kw)
-    return lib.flce_fwd_bwd(a["h"], a["W"], a["t"], a["N"], a["H"], a["V"], a["chunk"],
-                            a["loss"], a["gh"], a["gW"], a["ws"], a["wsb"], a["dt"],
-                            a["stream"])
+    return getattr(lib, entry)(a["h"], a["W"], a["t"], a["N"], a["H"], a["V"], a["chunk"],
+                               a["loss"], a["gh"], a["gW"], a["ws"], a["wsb"], a["dt"],
+                               a["stream"])
 
 
+@pytest.mark.parametrize("entry", ENTRY)
 @pytest.mark.parametrize("field", ["h", "W", "t", "loss", "gh", "gW", "ws"])
-def test_null_pointer_is_invalid(lib, field):
-    assert _call(lib, **{field: None}) == INVALID
+def test_null_pointer_is_invalid(lib, entry, field):
+    assert _call(lib, entry, **{field: None}) == INVALID
 
 
+@pytest.mark.parametrize("entry", ENTRY)
 @pytest.mark.parametrize("field,value", [("N", 0), ("N", -3), ("H", 0), ("V", 0),
                                          ("chunk", 0), ("N", 1 << 31), ("dt", 2)])
-def test_bad_sizes_are_invalid(lib, field, value):
-    assert _call(lib, **{field: value}) == INVALID
+def test_bad_sizes_are_invalid(lib, entry, field, value):
+    assert _call(lib, entry, **{field: value}) == INVALID
 
 
+@pytest.mark.parametrize("entry", ENTRY)
 @pytest.mark.parametrize("H", [1, 4, 12, 4095])
-def test_hidden_not_multiple_of_8_is_unsupported(lib, H):
-    assert _call(lib, H=H) == UNSUPPORTED
+def test_hidden_not_multiple_of_8_is_unsupported(lib, entry, H):
+    assert _call(lib, entry, H=H) == UNSUPPORTED
 
 
+@pytest.mark.parametrize("entry", ENTRY)
 @pytest.mark.parametrize("field", ["h", "W", "gh", "gW", "ws"])
-def test_misaligned_pointer_is_unsupported(lib, field):
-    assert _call(lib, **{field: P + 8}) == UNSUPPORTED
+def test_misaligned_pointer_is_unsupported(lib, entry, field):
+    assert _call(lib, entry, **{field: P + 8}) == UNSUPPORTED
+
+
+def test_scale_grads_validates(lib):
+    f = lib.flce_scale_grads
+    assert f(P, 4, P, 4, None, BF16, None) == INVALID            # no scale
+    assert f(P, -1, P, 4, P, BF16, None) == INVALID              # negative count
+    assert f(None, 4, P, 4, P, BF16, None) == INVALID            # buffer missing
+    assert f(P, 4, None, 4, P, F32, None) == INVALID
+    assert f(P, 4, P, 4, P, 7, None) == INVALID                  # dtype
+    assert f(P + 8, 4, P, 4, P, BF16, None) == UNSUPPORTED       # alignment
+    assert f(P, 4, P + 4, 4, P, BF16, None) == UNSUPPORTED
+    assert f(P, 4, P, 4, P + 2, BF16, None) == UNSUPPORTED
 
 
 def test_launch_count(lib):
