@@ -181,6 +181,28 @@ flce_status flce_ce_rows(float* z, int64_t ldz, const int32_t* targets,
                          float* row_loss, int64_t loss_stride, flce_dtype dt,
                          hipStream_t stream);
 
+/*
+ * Cross entropy on given logits, the gradient written over them (page 3,
+ * "Complete Guide to Liger Kernel", section "LigerCrossEntropyLoss": the
+ * loss of [B*S, V] logits against labels, computed chunk-wise with the
+ * gradient formed in the same pass): for the `rows` rows of `logits`
+ * (dt: bf16 or fp32, row pitch ld >= V elements)
+ *   *loss      = (1/rows) sum_i (logsumexp_j z[i, j] - z[i, t_i])   (fp32)
+ *   row_loss[i] = logsumexp_j z[i, j] - z[i, t_i]   [rows] fp32, caller-owned
+ *   z[i, j]   <- (softmax(z[i, :])_j - [j == t_i]) / rows, in place, same
+ *               dtype and positions (bf16 rounded to nearest even)
+ * i.e. the logits become dloss/dlogits of the mean loss.  Two passes over
+ * each row (max / sum, then the rewrite), one wave64 per row; the mean is
+ * summed in fp64 in a fixed order.  logits must be aligned to its element
+ * size (16 bytes with ld % 8 == 0 for bf16, resp. ld % 4 == 0 for fp32,
+ * selects the vector path); targets 0 <= t < V (an out-of-range target is
+ * never dereferenced and makes the loss NaN).  Null pointers or bad sizes
+ * give FLCE_ERR_INVALID_ARG, misalignment FLCE_ERR_UNSUPPORTED.
+ */
+flce_status flce_cross_entropy(void* logits, int64_t ld, const int32_t* targets,
+                               int64_t rows, int64_t V, float* loss, float* row_loss,
+                               flce_dtype dt, hipStream_t stream);
+
 /* A static, human-readable name for a status code (host only). */
 const char* flce_status_string(flce_status s);
 

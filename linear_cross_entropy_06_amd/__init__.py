@@ -5,6 +5,7 @@ include/flce.h); this package is its Python binding.
 """
 
 from ._lib import (
+    CrossEntropyFunction,
     EXPORTS,
     FLCE_BF16,
     FLCE_F32,
@@ -15,6 +16,8 @@ from ._lib import (
     LinearCrossEntropyFunction,
     STEP_NAMES,
     ce_rows,
+    cross_entropy,
+    cross_entropy_,
     fwd_bwd,
     launch_count,
     linear_cross_entropy,
@@ -25,6 +28,7 @@ from ._lib import (
 )
 
 __all__ = [
+    "CrossEntropyFunction",
     "EXPORTS",
     "FLCE_BF16",
     "FLCE_F32",
@@ -35,6 +39,8 @@ __all__ = [
     "LinearCrossEntropyFunction",
     "STEP_NAMES",
     "ce_rows",
+    "cross_entropy",
+    "cross_entropy_",
     "fwd_bwd",
     "launch_count",
     "linear_cross_entropy",

@@ -39,6 +39,7 @@ EXPORTS = (
     "flce_fwd_bwd_timed",
     "flce_logits",
     "flce_ce_rows",
+    "flce_cross_entropy",
     "flce_status_string",
 )
 
@@ -84,6 +85,8 @@ def load() -> ctypes.CDLL:
     lib.flce_ce_rows.argtypes = [vp, i64, vp, i64, i64, ctypes.c_float, vp, i64,
                                  ctypes.c_int, vp]
     lib.flce_ce_rows.restype = ctypes.c_int
+    lib.flce_cross_entropy.argtypes = [vp, i64, vp, i64, i64, vp, vp, ctypes.c_int, vp]
+    lib.flce_cross_entropy.restype = ctypes.c_int
     lib.flce_status_string.argtypes = [ctypes.c_int]
     lib.flce_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -297,3 +300,58 @@ def linear_cross_entropy(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor
     """Mean cross entropy of h W^T against int32 targets as a differentiable
     op (the logits are never materialised)."""
     return LinearCrossEntropyFunction.apply(h, W, targets, chunk)
+
+
+def cross_entropy_(logits: torch.Tensor, targets: torch.Tensor,
+                   loss: Optional[torch.Tensor] = None,
+                   row_loss: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Mean cross entropy of 2-D ``logits`` (bf16 or fp32) against int32
+    ``targets`` via ``flce_cross_entropy``; ``logits`` is overwritten with
+    dloss/dlogits (the trailing underscore: in place).  Returns the loss."""
+    lib = load()
+    _need_cuda(targets)
+    if not logits.is_cuda or logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be a 2-D GPU tensor with unit column stride")
+    if targets.dtype != torch.int32:
+        raise TypeError("targets must be int32")
+    rows, V = logits.shape
+    dev = logits.device
+    if loss is None:
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+    if row_loss is None:
+        row_loss = torch.empty(rows, dtype=torch.float32, device=dev)
+    _need_cuda(loss, row_loss)
+    _check(lib.flce_cross_entropy(logits.data_ptr(), logits.stride(0), targets.data_ptr(), rows,
+                                  V, loss.data_ptr(), row_loss.data_ptr(), _dt(logits),
+                                  _stream_ptr(dev)))
+    return loss
+
+
+class CrossEntropyFunction(torch.autograd.Function):
+    """Autograd node for the cross entropy on given logits: the forward call
+    computes the mean loss and turns the logits' own memory into their
+    gradient (the logits tensor is consumed); backward scales it by the
+    incoming gradient of the loss.  One backward per forward."""
+
+    @staticmethod
+    def forward(ctx, logits, targets):
+        buf = logits.detach()
+        loss = cross_entropy_(buf, targets)
+        ctx.save_for_backward(buf)
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        (g,) = ctx.saved_tensors
+        scale = grad_out.detach().to(torch.float32).reshape(1).contiguous()
+        if g.dtype == torch.float32:
+            scale_grads(None, g.view(-1), scale)
+        else:
+            scale_grads(g.view(-1), None, scale)
+        return g, None
+
+
+def cross_entropy(logits: torch.Tensor, targets: torch.Tensor) -> torch.Tensor:
+    """Differentiable mean cross entropy on given logits; the logits' memory
+    holds their gradient afterwards (do not reuse the logits)."""
+    return CrossEntropyFunction.apply(logits, targets)

@@ -289,6 +289,86 @@ ce_rows_exp_kernel(uint16_t* __restrict__ u, int64_t ldu, const float* __restric
   }
 }
 
+// Cross entropy of given bf16 logit rows (the standalone loss on logits):
+// pass 1 online (max, sum) over the row, pass 2 rewrites every logit in
+// place with (2^(y - lse2) - [j == t]) * scale in bf16 (same place, same
+// size).  VEC: rows start 16-byte aligned and 8 logits move per lane and
+// step; otherwise one logit per lane and step.
+template <bool VEC, int UNROLL>
+__global__ void __launch_bounds__(64 * kWavesPerBlock)
+ce_rows_bf16_kernel(uint16_t* __restrict__ z, int64_t ldz, const int32_t* __restrict__ targets,
+                    int rows, int V, float scale, float* __restrict__ row_loss,
+                    int64_t loss_stride) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  uint16_t* zr = z + (int64_t)row * ldz;
+  const int t = targets[row];
+  const bool t_ok = (t >= 0) && (t < V);
+  const float zt = t_ok ? __uint_as_float((uint32_t)zr[t] << 16) : __builtin_nanf("");
+
+  float m = -INFINITY, s = 0.0f;
+  const int nvec = VEC ? V >> 3 : 0;
+  const u32x4* zv = reinterpret_cast<const u32x4*>(zr);
+  if constexpr (VEC) {
+    for (int v0 = 0; v0 < nvec; v0 += 64 * UNROLL) {
+      u32x4 x[UNROLL];
+#pragma unroll
+      for (int k = 0; k < UNROLL; ++k)
+        if (v0 + lane + 64 * k < nvec) x[k] = zv[v0 + lane + 64 * k];
+#pragma unroll
+      for (int k = 0; k < UNROLL; ++k) {
+        if (v0 + lane + 64 * k >= nvec) continue;
+        online_add4(f32x4{bf16_lo(x[k][0]), bf16_hi(x[k][0]), bf16_lo(x[k][1]),
+                          bf16_hi(x[k][1])}, m, s);
+        online_add4(f32x4{bf16_lo(x[k][2]), bf16_hi(x[k][2]), bf16_lo(x[k][3]),
+                          bf16_hi(x[k][3])}, m, s);
+      }
+    }
+  }
+  for (int j = 8 * nvec + lane; j < V; j += 64)
+    online_add(to_log2(__uint_as_float((uint32_t)zr[j] << 16)), m, s);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off, 64);
+    const float s2 = __shfl_xor(s, off, 64);
+    combine(m, s, m2, s2);
+  }
+  const float lse2 = m + log2_hw(s);
+  if (lane == 0)
+    row_loss[(int64_t)row * loss_stride] = ((m - to_log2(zt)) + log2_hw(s)) * kLn2;
+
+  if constexpr (VEC) {
+    u32x4* zw = reinterpret_cast<u32x4*>(zr);
+    for (int v0 = 0; v0 < nvec; v0 += 64 * UNROLL) {
+      u32x4 x[UNROLL];
+#pragma unroll
+      for (int k = 0; k < UNROLL; ++k)
+        if (v0 + lane + 64 * k < nvec) x[k] = zw[v0 + lane + 64 * k];
+#pragma unroll
+      for (int k = 0; k < UNROLL; ++k) {
+        const int v = v0 + lane + 64 * k;
+        if (v >= nvec) continue;
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 8 * v + 2 * e;
+          const float g0 =
+              (exp2_hw(to_log2(bf16_lo(x[k][e])) - lse2) - (j == t ? 1.0f : 0.0f)) * scale;
+          const float g1 =
+              (exp2_hw(to_log2(bf16_hi(x[k][e])) - lse2) - (j + 1 == t ? 1.0f : 0.0f)) * scale;
+          w[e] = pack_bf16x2(g0, g1);
+        }
+        zw[v] = w;
+      }
+    }
+  }
+  for (int j = 8 * nvec + lane; j < V; j += 64) {
+    const float p = exp2_hw(to_log2(__uint_as_float((uint32_t)zr[j] << 16)) - lse2);
+    zr[j] = (uint16_t)bf16_bits((p - (j == t ? 1.0f : 0.0f)) * scale);
+  }
+}
+
 constexpr int kSumThreads = 256;
 
 __global__ void __launch_bounds__(kSumThreads)
@@ -331,6 +411,22 @@ hipError_t launch_ce_rows(float* z, int64_t ldz, const int32_t* targets, int row
                        rows, V, scale, row_loss, loss_stride);
   else
     hipLaunchKernelGGL((ce_rows_kernel<false, false>), grid, block, 0, s, z, ldz, targets,
+                       rows, V, scale, row_loss, loss_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_rows_bf16(uint16_t* z, int64_t ldz, const int32_t* targets, int rows,
+                               int V, float scale, float* row_loss, int64_t loss_stride,
+                               hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((rows + kWavesPerBlock - 1) / kWavesPerBlock);
+  const dim3 block(64 * kWavesPerBlock);
+  const bool vec = ((ldz & 7) == 0) && ((reinterpret_cast<uintptr_t>(z) & 15) == 0);
+  if (vec)
+    hipLaunchKernelGGL((ce_rows_bf16_kernel<true, 4>), grid, block, 0, s, z, ldz, targets, rows,
+                       V, scale, row_loss, loss_stride);
+  else
+    hipLaunchKernelGGL((ce_rows_bf16_kernel<false, 4>), grid, block, 0, s, z, ldz, targets,
                        rows, V, scale, row_loss, loss_stride);
   return hipGetLastError();
 }

@@ -265,6 +265,30 @@ extern "C" flce_status flce_ce_rows(float* z, int64_t ldz, const int32_t* target
              : FLCE_ERR_HIP;
 }
 
+extern "C" flce_status flce_cross_entropy(void* logits, int64_t ld, const int32_t* targets,
+                                          int64_t rows, int64_t V, float* loss,
+                                          float* row_loss, flce_dtype dt, hipStream_t stream) {
+  if (!logits || !targets || !loss || !row_loss) return FLCE_ERR_INVALID_ARG;
+  if (!dims_ok(rows) || !dims_ok(V) || ld < V || !dtype_ok(dt)) return FLCE_ERR_INVALID_ARG;
+  const uintptr_t es_mask = dt == FLCE_BF16 ? 1u : 3u;
+  if ((reinterpret_cast<uintptr_t>(logits) & es_mask) ||
+      (reinterpret_cast<uintptr_t>(targets) & 3u) ||
+      (reinterpret_cast<uintptr_t>(row_loss) & 3u) || (reinterpret_cast<uintptr_t>(loss) & 3u))
+    return FLCE_ERR_UNSUPPORTED;
+  const float inv = static_cast<float>(1.0 / static_cast<double>(rows));
+  const int r = static_cast<int>(rows);
+  hipError_t e =
+      dt == FLCE_BF16
+          ? flce::launch_ce_rows_bf16(static_cast<uint16_t*>(logits), ld, targets, r,
+                                      static_cast<int>(V), inv, row_loss, 1, stream)
+          : flce::launch_ce_rows(static_cast<float*>(logits), ld, targets, r,
+                                 static_cast<int>(V), inv, row_loss, 1, false, stream);
+  if (e != hipSuccess) return FLCE_ERR_HIP;
+  return flce::launch_loss_sum(row_loss, 1, r, inv, 1, loss, stream) == hipSuccess
+             ? FLCE_OK
+             : FLCE_ERR_HIP;
+}
+
 extern "C" const char* flce_status_string(flce_status s) {
   switch (s) {
     case FLCE_OK: return "FLCE_OK";

@@ -77,6 +77,12 @@ hipError_t launch_ce_rows(float* z, int64_t ldz, const int32_t* targets,
                           int rows, int V, float scale, float* row_loss,
                           int64_t loss_stride, bool out_bf16, hipStream_t s);
 
+// The same on bf16 logits at pitch ldz elements, rewritten in place as the
+// bf16 gradient (same positions).
+hipError_t launch_ce_rows_bf16(uint16_t* z, int64_t ldz, const int32_t* targets, int rows,
+                               int V, float scale, float* row_loss, int64_t loss_stride,
+                               hipStream_t s);
+
 // The same from exponentiated logits (kExpBF16 output u at pitch ldu, with
 // its (max, sum) pairs): u is rewritten in place as the bf16 gradient.  The
 // target logit of row i is recomputed as the dot product of h[i] and

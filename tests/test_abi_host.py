@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
     assert names == sorted(["flce_workspace_bytes", "flce_fwd_bwd", "flce_launch_count",
                             "flce_fwd_bwd_timed", "flce_logits", "flce_ce_rows",
                             "flce_fwd_bwd_accumulate", "flce_scale_grads",
-                            "flce_status_string"])
+                            "flce_cross_entropy", "flce_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -152,6 +152,20 @@ def test_step_entry_points_validate(lib):
     assert lib.flce_ce_rows(P, 4, P, 4, 5, ctypes.c_float(1.0), P, 1, BF16, None) == INVALID
     assert lib.flce_ce_rows(P + 2, 8, P, 4, 5, ctypes.c_float(1.0), P, 1, BF16,
                             None) == UNSUPPORTED
+
+
+def test_cross_entropy_validates(lib):
+    f = lib.flce_cross_entropy
+    assert f(None, 8, P, 4, 5, P, P, BF16, None) == INVALID
+    assert f(P, 8, None, 4, 5, P, P, BF16, None) == INVALID
+    assert f(P, 8, P, 4, 5, None, P, BF16, None) == INVALID
+    assert f(P, 8, P, 4, 5, P, None, BF16, None) == INVALID
+    assert f(P, 4, P, 4, 5, P, P, BF16, None) == INVALID       # ld < V
+    assert f(P, 8, P, 0, 5, P, P, BF16, None) == INVALID       # rows
+    assert f(P, 8, P, 4, 5, P, P, 3, None) == INVALID          # dtype
+    assert f(P + 1, 8, P, 4, 5, P, P, BF16, None) == UNSUPPORTED
+    assert f(P + 2, 8, P, 4, 5, P, P, F32, None) == UNSUPPORTED
+    assert f(P, 8, P + 2, 4, 5, P, P, BF16, None) == UNSUPPORTED
 
 
 def test_status_strings(lib):
