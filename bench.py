@@ -52,6 +52,9 @@ def parse_args():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    p.add_argument("--op", choices=("flce", "ce"), default="flce",
+                   help="flce: the fused head (default); ce: cross entropy on given bf16 "
+                        "logits [1024, 128256] (flce_cross_entropy)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="first run one elementwise fp32 copy of this many MiB (a kernel of "
                         "known traffic, used to scale FETCH_SIZE/WRITE_SIZE counters)")
@@ -108,8 +111,90 @@ def cpu_baseline(inp, cfg, sample_tokens: int, chunk: int):
     }
 
 
+def bench_ce(args) -> int:
+    """Cross entropy on given logits: p3's [B*S, V] = [1024, 128256] bf16
+    logits (std 2, seeded), one flce_cross_entropy call per step (the call
+    rewrites the logits in place with their gradient; later steps run on
+    that buffer, the same work).  HBM-bound: each call reads the logits
+    twice and writes them once."""
+    import numpy as np
+    import torch
+
+    import linear_cross_entropy_06_amd as flce
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    flce.load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    rows, V = 1024, 128256
+    g = torch.Generator().manual_seed(args.seed)
+    z_cpu = (torch.randn(rows, V, generator=g) * 2.0).to(torch.bfloat16)
+    t_cpu = torch.randint(0, V, (rows,), generator=g, dtype=torch.int32)
+    z, t = z_cpu.to(dev), t_cpu.to(dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    row_loss = torch.empty(rows, dtype=torch.float32, device=dev)
+    first = flce.cross_entropy_(z, t, loss=loss, row_loss=row_loss)
+    loss0 = float(first)
+    for _ in range(args.warmup):
+        flce.cross_entropy_(z, t, loss=loss, row_loss=row_loss)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        flce.cross_entropy_(z, t, loss=loss, row_loss=row_loss)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    bytes_per = rows * V * 2 * 3 + rows * 8
+    out = {
+        "metric": "cross entropy on given logits: rows/s",
+        "value": rows / (ms * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0, 2^2) logits, uniform targets)",
+        "config": {"workload": "ce_on_logits_llama3_vocab", "rows": rows, "V": V},
+        "loss_first_call": loss0,
+        "roofline": {
+            "kernel": "ce_rows_bf16 (+ loss_sum)", "bound": "hbm",
+            "achieved": bytes_per / (ev_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": bytes_per / (ev_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+            "work_per_launch": f"{rows}*{V}*2*3 B (logits read twice, written once) "
+                               f"= {bytes_per:.4e} B",
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        S = 256
+        Z = z_cpu[:S].to(torch.float64).numpy()
+        tt = t_cpu[:S].numpy().astype(np.int64)
+        c0 = time.perf_counter()
+        oracle.row_losses(Z, tt)
+        oracle.dlogits(Z, tt, rows)
+        dt = time.perf_counter() - c0
+        out["cpu_baseline"] = {
+            "value": S / dt, "unit": "rows/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"first {S} of {rows} rows, fp64 numpy row_losses + dlogits: {dt:.2f} s"}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
+    if args.op == "ce":
+        if args.gpus != 1:
+            print("bench.py: this build runs on one GPU only", file=sys.stderr)
+            return 2
+        return bench_ce(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
