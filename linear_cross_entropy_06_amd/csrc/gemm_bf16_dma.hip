@@ -38,6 +38,8 @@
 //    results are never stored.
 #include "flce_internal.h"
 
+#include <type_traits>
+
 namespace flce {
 namespace {
 
@@ -408,70 +410,78 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
       // the (max, sum) pair.  Lanes l and l ^ 32 hold the two halves of
       // every 32-row block, so one shuffle completes a column over the
       // wave's 128 rows.
-      constexpr float kL2e = 1.4426950408889634f;
-      const int hl = lane >> 5;
-      float mneg[4], ssum[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float mz = -__builtin_inff();
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (m0 + wm * 128 + i * 32 + 8 * q + 4 * hl < g.M)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) mz = fmaxf(mz, acc[i][j][4 * q + e]);
-        mz = fmaxf(mz, __shfl_xor(mz, 32, 64));
-        // No row of this half tile below M: nothing is stored for it.
-        mneg[j] = mz == -__builtin_inff() ? 0.0f : -to_log2(mz);
-        ssum[j] = 0.0f;
-      }
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-          const int i = 2 * p + ii;
-#pragma unroll
+      // Tiles wholly inside the output skip every per-element edge test.
+      auto exp_body = [&](auto guard_tag) __attribute__((always_inline)) {
+        constexpr bool kGuard = decltype(guard_tag)::value;
+        constexpr float kL2e = 1.4426950408889634f;
+        const int hl = lane >> 5;
+        float mneg[4], ssum[4];
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float mz = -__builtin_inff();
+  #pragma unroll
+          for (int i = 0; i < 4; ++i)
+  #pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (!kGuard || m0 + wm * 128 + i * 32 + 8 * q + 4 * hl < g.M)
+  #pragma unroll
+                for (int e = 0; e < 4; ++e) mz = fmaxf(mz, acc[i][j][4 * q + e]);
+          mz = fmaxf(mz, __shfl_xor(mz, 32, 64));
+          // No row of this half tile below M: nothing is stored for it.
+          mneg[j] = mz == -__builtin_inff() ? 0.0f : -to_log2(mz);
+          ssum[j] = 0.0f;
+        }
+  #pragma unroll
+        for (int p = 0; p < 2; ++p) {
+  #pragma unroll
+          for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * p + ii;
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int nl = 32 * j + (lane & 31);
+  #pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const bool ok = !kGuard || m0 + wm * 128 + i * 32 + 8 * q + 4 * hl < g.M;
+                float u[4];
+  #pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  u[e] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * q + e], kL2e,
+                                                                     mneg[j]))
+                            : 0.0f;
+                ssum[j] += (u[0] + u[1]) + (u[2] + u[3]);
+                const u32x2 w = {pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3])};
+                *reinterpret_cast<u32x2*>(buf + lds_off(nl, 4 * ii + q) + 8 * hl) = w;
+              }
+            }
+          }
+          const int m = m0 + wm * 128 + 64 * p + 8 * c_rd;
+  #pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const int nl = 8 * t + (lane >> 3);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(buf + lds_off(nl, c_rd));
+            const int n = n0 + wn * 128 + nl;
+            if (!kGuard || (n < g.N && m < g.M))  // M % 8 == 0: runs of 8 all in or out
+              *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.out) + (int64_t)n * g.ldo + m) = v;
+          }
+        }
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) ssum[j] += __shfl_xor(ssum[j], 32, 64);
+        if (lane < 32 && m0 + wm * 128 < g.M) {
+  #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int nl = 32 * j + (lane & 31);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const bool ok = m0 + wm * 128 + i * 32 + 8 * q + 4 * hl < g.M;
-              float u[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                u[e] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * q + e], kL2e,
-                                                                   mneg[j]))
-                          : 0.0f;
-              ssum[j] += (u[0] + u[1]) + (u[2] + u[3]);
-              const u32x2 w = {pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3])};
-              *reinterpret_cast<u32x2*>(buf + lds_off(nl, 4 * ii + q) + 8 * hl) = w;
+            const int n = n0 + wn * 128 + 32 * j + lane;
+            if (!kGuard || n < g.N) {
+              float* pr = g.row_part + (int64_t)n * g.ldp + 2 * (2 * tmi + wm);
+              pr[0] = -mneg[j];
+              pr[1] = ssum[j];
             }
           }
         }
-        const int m = m0 + wm * 128 + 64 * p + 8 * c_rd;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int nl = 8 * t + (lane >> 3);
-          const u32x4 v = *reinterpret_cast<const u32x4*>(buf + lds_off(nl, c_rd));
-          const int n = n0 + wn * 128 + nl;
-          if (n < g.N && m < g.M)  // M % 8 == 0: a run of 8 is all in or all out
-            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.out) + (int64_t)n * g.ldo + m) = v;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ssum[j] += __shfl_xor(ssum[j], 32, 64);
-      if (lane < 32 && m0 + wm * 128 < g.M) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = n0 + wn * 128 + 32 * j + lane;
-          if (n < g.N) {
-            float* pr = g.row_part + (int64_t)n * g.ldp + 2 * (2 * tmi + wm);
-            pr[0] = -mneg[j];
-            pr[1] = ssum[j];
-          }
-        }
-      }
+      };
+      if (m0 + kBM <= g.M && n0 + kBN <= g.N)
+        exp_body(std::integral_constant<bool, false>{});
+      else
+        exp_body(std::integral_constant<bool, true>{});
     } else {
       // fp32 output: one 32(m) x 128(n) block i at a time, double-buffered.
       const bool accumulate = EPI == kAccumF32 && g.beta;
