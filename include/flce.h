@@ -64,7 +64,12 @@ typedef enum flce_status {
  *   bf16 inputs, H % 64 == 0, V % 8 == 0:
  *        C * V * 2 + C * ceil(V / 128) * 8   (the logits of one token chunk
  *        kept as bf16 exponentials, plus two floats per row and 128-column
- *        slice)
+ *        slice; each region rounded up to 256 bytes)
+ *        + P * H * 4 when chunks are short: if a chunk of r rows gives the
+ *        H x r grad_h product <= 128 tiles of 256 x 256 (and V % 64 == 0,
+ *        V >= 1024 per part), its K = V contraction is split into s = 2
+ *        (<= 128 tiles) or 4 (<= 64) fp32 parts, and P is the larger of
+ *        s * r over r = C and r = N mod C
  *   otherwise:
  *        C * V * 4                           (the fp32 logits of one chunk)
  * (FLCE_GEMM_GENERIC=1 in the environment, which switches the direct-to-LDS

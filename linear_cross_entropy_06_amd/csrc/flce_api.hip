@@ -51,15 +51,51 @@ inline bool exp_path(int64_t H, int64_t V, flce_dtype dt) {
 // (max, sum) pairs per row on the exponentiated path.
 inline int64_t n_half_tiles(int64_t V) { return (V + flce::kHalfTile - 1) / flce::kHalfTile; }
 
+// K split of the grad_h contraction (H x rows output, K = V) when its
+// 256 x 256 tiles would not fill the chip: 4 parts for <= 64 tiles, 2 for
+// <= 128 (exponentiated path with V % 64 == 0, at least 16 slabs a part).
+inline int grad_h_splits(int64_t H, int64_t rows, int64_t V) {
+  const int64_t tiles = ((H + 255) / 256) * ((rows + 255) / 256);
+  const int s = tiles <= 64 ? 4 : tiles <= 128 ? 2 : 1;
+  return (V % 64 == 0 && V / 64 >= 16 * s) ? s : 1;
+}
+
+// Rows of the fp32 [rows][H] part buffer the K split needs: the larger of
+// splits(rows) * rows over the chunk sizes that occur (C, and N mod C).
+inline int64_t split_scratch_rows(int64_t N, int64_t H, int64_t C, int64_t V) {
+  int64_t best = 0;
+  for (int64_t r : {C, N % C}) {
+    if (r <= 0) continue;
+    const int s = grad_h_splits(H, r, V);
+    if (s > 1 && s * r > best) best = s * r;
+  }
+  return best;
+}
+
+inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Byte offsets of the exponentiated path's workspace regions.
+struct ExpLayout {
+  int64_t pairs, parts, total;
+};
+inline ExpLayout exp_layout(int64_t N, int64_t C, int64_t H, int64_t V) {
+  ExpLayout l;
+  l.pairs = round_up(C * V * 2, 256);
+  l.parts = round_up(l.pairs + C * n_half_tiles(V) * 8, 256);
+  l.total = l.parts + split_scratch_rows(N, H, C, V) * H * 4;
+  return l;
+}
+
 }  // namespace
 
 extern "C" size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk,
                                        flce_dtype dt) {
   if (!dims_ok(N) || !dims_ok(H) || !dims_ok(V) || chunk < 1 || !dtype_ok(dt)) return 0;
-  const size_t C = static_cast<size_t>(chunk < N ? chunk : N);
-  if (exp_path(H, V, dt))  // bf16 logits of one chunk + 2 floats per row and half tile
-    return C * static_cast<size_t>(V) * 2u + C * static_cast<size_t>(n_half_tiles(V)) * 8u;
-  return C * static_cast<size_t>(V) * 4u;  // fp32 logits of one chunk
+  const int64_t C = chunk < N ? chunk : N;
+  // bf16 logits of one chunk + 2 floats per row and half tile (+ grad_h
+  // K-split parts for short chunks)
+  if (exp_path(H, V, dt)) return static_cast<size_t>(exp_layout(N, C, H, V).total);
+  return static_cast<size_t>(C) * static_cast<size_t>(V) * 4u;  // fp32 logits of one chunk
 }
 
 extern "C" int64_t flce_launch_count(int64_t N, int64_t chunk) {
@@ -117,7 +153,9 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
   float* z = static_cast<float*>(workspace);
   uint16_t* u = static_cast<uint16_t*>(workspace);
   const int64_t ldp = 2 * n_half_tiles(V);
-  float* pairs = reinterpret_cast<float*>(static_cast<char*>(workspace) + C * V * 2);
+  const ExpLayout lay = exp_layout(N, C, H, V);
+  float* pairs = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.pairs);
+  float* parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.parts);
   void* g_base = workspace;
   const int64_t loss_stride = H * es / 4;  // floats between staged row losses
 
@@ -165,11 +203,26 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
 
     // 4. grad_h_c^T = W^T . G^T: A(m = hidden, k = vocab) = W[k][m],
     //    B(n = token, k = vocab) = G[n][k].
+    //    Few output tiles (short chunks): K split into fp32 parts in the
+    //    workspace, then summed into grad_h in a fixed order (both launches
+    //    are this step).
     flce::GemmArgs g4{W, H, g_base, ldg, ghc, H, static_cast<int>(H), rows, static_cast<int>(V),
                       0};
     g4.group_m = 4;
+    const int splits = expo ? grad_h_splits(H, rows, V) : 1;
     mk.before();
-    e = gemm(dt, false, true, flce::kStoreOut, vec, g4, stream);
+    if (splits > 1) {
+      g4.out = parts;
+      g4.splits = splits;
+      g4.split_stride = static_cast<int64_t>(rows) * H;
+      e = flce::launch_gemm_bf16(false, true, flce::kStoreF32, vec, g4, stream);
+      if (e == hipSuccess)
+        e = flce::launch_sum_parts_bf16(parts, splits, static_cast<int64_t>(rows) * H,
+                                        reinterpret_cast<uint16_t*>(ghc),
+                                        static_cast<int64_t>(rows) * H, stream);
+    } else {
+      e = gemm(dt, false, true, flce::kStoreOut, vec, g4, stream);
+    }
     mk.after();
     if (e != hipSuccess) return FLCE_ERR_HIP;
 

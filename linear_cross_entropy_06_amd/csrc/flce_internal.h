@@ -46,6 +46,11 @@ struct GemmArgs {
   // (max, sum) pairs of the kExpBF16 epilogue; ldp in floats.
   float* row_part = nullptr;
   int64_t ldp = 0;
+  // K split (direct-to-LDS kernel): the K slabs are cut into `splits`
+  // consecutive parts; part s is computed by its own workgroups and stored
+  // at out + s * split_stride (elements), to be summed by the caller.
+  int splits = 1;
+  int64_t split_stride = 0;
 };
 
 // bf16 operands, MFMA 32x32x16, fp32 accumulation.  `vec` selects the
@@ -91,6 +96,11 @@ hipError_t launch_ce_rows_exp(uint16_t* u, int64_t ldu, const float* row_part, i
                               const uint16_t* h, const uint16_t* W, int H,
                               const int32_t* targets, int rows, int V, float scale,
                               float* row_loss, int64_t loss_stride, hipStream_t s);
+
+// out[i] = bf16(sum over s < S of parts[s * stride + i]) for i < n, summed
+// in the order s = 0, 1, ... (deterministic); parts and out 16-byte aligned.
+hipError_t launch_sum_parts_bf16(const float* parts, int S, int64_t stride, uint16_t* out,
+                                 int64_t n, hipStream_t st);
 
 // x[0 .. n) *= *s in place (bf16 with round to nearest even, or fp32); x
 // 16-byte aligned, s a device pointer.

@@ -366,8 +366,8 @@ hipError_t launch_gemm_bf16(bool a_kc, bool b_kc, int epi, bool vec,
   // the larger operand stays in L2 across consecutive tiles.
   const int m_fastest = g.M < g.N ? 1 : 0;
   if (gemm_bf16_uses_dma(a_kc, b_kc, vec, g)) return launch_gemm_bf16_dma(a_kc, b_kc, epi, g, s);
-  // Exponentiated logits are produced by the direct-to-LDS kernel only.
-  if (epi == kExpBF16) return hipErrorInvalidValue;
+  // Exponentiated logits and K splits exist on the direct-to-LDS kernel only.
+  if (epi == kExpBF16 || g.splits > 1) return hipErrorInvalidValue;
   if (a_kc && b_kc && epi == kStoreF32)       // logits
     return launch_layout<true, true, kStoreF32, float>(vec, g, m_fastest, s);
   if (!a_kc && b_kc && epi == kStoreOut)      // grad_h (bf16 out)

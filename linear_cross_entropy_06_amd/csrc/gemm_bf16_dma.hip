@@ -252,6 +252,19 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
   const int tni = r / gsize;
   const int m0 = tmi * kBM, n0 = tni * kBN;
 
+  // K split: workgroup row blockIdx.y takes its own run of slabs and its own
+  // output slice.
+  int KT = g.K / kBK;
+  if (g.splits > 1) {
+    const int per = (KT + g.splits - 1) / g.splits;
+    const int kt0 = (int)blockIdx.y * per;
+    KT = min(per, KT - kt0);  // >= 1: checked on the host
+    const int64_t k0 = (int64_t)kt0 * kBK;
+    g.A = static_cast<const uint16_t*>(g.A) + (A_KC ? k0 : k0 * g.lda);
+    g.B = static_cast<const uint16_t*>(g.B) + (B_KC ? k0 : k0 * g.ldb);
+    g.out = static_cast<OutT*>(g.out) + (int64_t)blockIdx.y * g.split_stride;
+  }
+
   DmaOperand<A_KC> da;
   DmaOperand<B_KC> db;
   da.init(static_cast<const uint16_t*>(g.A), g.lda, m0, g.M, wave, lane);
@@ -269,7 +282,6 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int KT = g.K / kBK;
   da.kt_total = db.kt_total = KT;
   da.start = db.start = g.stagger > 0 ? (int)(((unsigned)grp * (unsigned)g.stagger) % (unsigned)KT) : 0;
   // Prologue: A_0 -> slot 0, B_0 -> slot 1, A_1 -> slot 2; wait for the
@@ -530,8 +542,9 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
   const int tiles_n = (g.N + kBN - 1) / kBN;
   int gm = g.group_m > 0 ? g.group_m : 4;
   if (gm > tiles_m) gm = tiles_m;
-  hipLaunchKernelGGL((gemm_bf16_dma_kernel<A_KC, B_KC, EPI, OutT>), dim3(tiles_m * tiles_n),
-                     dim3(256), 0, s, g, gm);
+  hipLaunchKernelGGL((gemm_bf16_dma_kernel<A_KC, B_KC, EPI, OutT>),
+                     dim3(tiles_m * tiles_n, g.splits > 1 ? g.splits : 1), dim3(256), 0, s, g,
+                     gm);
   return hipGetLastError();
 }
 
@@ -546,6 +559,10 @@ bool gemm_bf16_dma_supported(bool a_kc, bool b_kc, const GemmArgs& g) {
   // Operand pieces are addressed by 32-bit offsets within 256 rows (k-
   // contiguous) or 64 k-rows (m-contiguous) of a leading dimension.
   if (g.lda >= (int64_t{1} << 22) || g.ldb >= (int64_t{1} << 22)) return false;
+  if (g.splits > 1) {  // every part gets at least one slab
+    const int kt = g.K / kBK, per = (kt + g.splits - 1) / g.splits;
+    if ((g.splits - 1) * per >= kt || g.splits > 65535) return false;
+  }
   const uintptr_t al = reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B) |
                        reinterpret_cast<uintptr_t>(g.out);
   if (al & 15u) return false;
@@ -564,6 +581,8 @@ hipError_t launch_gemm_bf16_dma(bool a_kc, bool b_kc, int epi, const GemmArgs& g
   }
   if (!a_kc && b_kc && epi == kStoreOut)
     return launch_dma<false, true, kStoreOut, uint16_t>(g, s);
+  if (!a_kc && b_kc && epi == kStoreF32)  // K-split parts of grad_h
+    return launch_dma<false, true, kStoreF32, float>(g, s);
   if (!a_kc && !b_kc && epi == kAccumF32)
     return launch_dma<false, false, kAccumF32, float>(g, s);
   return hipErrorInvalidValue;

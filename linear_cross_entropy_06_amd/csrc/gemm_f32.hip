@@ -91,6 +91,7 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
 hipError_t launch_gemm_f32(bool a_kc, bool b_kc, int epi, const GemmArgs& g,
                            hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.splits > 1 || epi == kExpBF16) return hipErrorInvalidValue;  // bf16 kernel only
   if (a_kc && b_kc && (epi == kStoreF32 || epi == kStoreOut))
     return launch_one<true, true, kStoreF32>(g, s);
   if (!a_kc && b_kc && (epi == kStoreF32 || epi == kStoreOut))

@@ -1,4 +1,7 @@
-// Scaling of precomputed gradients by the loss's upstream gradient (gfx950).
+// Elementwise kernels of the head (gfx950): scaling of precomputed
+// gradients by the loss's upstream gradient, and the sum of K-split parts.
+//
+// Scaling:
 //
 // The fused head forms dloss/dh and dloss/dW during the forward call (page
 // 1, "Liger Kernel explained", section "What does Liger Kernel actually
@@ -64,7 +67,38 @@ inline dim3 grid_for(int64_t n16) {
   return dim3(static_cast<unsigned>(g));
 }
 
+// out[i] = bf16(parts[i] + parts[stride + i] + ...), 4 values per thread and
+// step, parts summed in index order.
+__global__ void __launch_bounds__(kThreads)
+sum_parts_kernel(const float* __restrict__ parts, int S, int64_t stride,
+                 uint16_t* __restrict__ out, int64_t n4, int tail) {
+  for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * kThreads) {
+    f32x4 a = reinterpret_cast<const f32x4*>(parts)[i];
+    for (int s = 1; s < S; ++s) a += reinterpret_cast<const f32x4*>(parts + s * stride)[i];
+    uint2 w;
+    w.x = pack_bf16x2(a[0], a[1]);
+    w.y = pack_bf16x2(a[2], a[3]);
+    reinterpret_cast<uint2*>(out)[i] = w;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < tail) {
+    const int64_t i = n4 * 4 + threadIdx.x;
+    float a = parts[i];
+    for (int s = 1; s < S; ++s) a += parts[s * stride + i];
+    out[i] = (uint16_t)(pack_bf16x2(a, 0.0f) & 0xffffu);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_sum_parts_bf16(const float* parts, int S, int64_t stride, uint16_t* out,
+                                 int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t n4 = n / 4;
+  hipLaunchKernelGGL(sum_parts_kernel, grid_for(n4), dim3(kThreads), 0, st, parts, S, stride,
+                     out, n4, static_cast<int>(n % 4));
+  return hipGetLastError();
+}
 
 hipError_t launch_scale(void* x, int64_t n, bool bf16, const float* s, hipStream_t st) {
   if (n <= 0) return hipSuccess;

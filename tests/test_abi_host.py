@@ -55,9 +55,13 @@ def test_workspace_bytes(lib):
     # bf16 with H % 64 == 0 and V % 8 == 0: exponentiated bf16 logits of one
     # chunk plus two floats per row and 128-column half tile
     assert f(8192, 4096, 128256, 4096, BF16) == 4096 * 128256 * 2 + 4096 * 1002 * 8
-    assert f(8192, 4096, 128256, 2048, BF16) == 2048 * 128256 * 2 + 2048 * 1002 * 8
     assert f(8192, 3584, 256000, 4096, BF16) == 4096 * 256000 * 2 + 4096 * 2000 * 8
     assert f(300, 128, 1000, 128, BF16) == 128 * 1000 * 2 + 128 * 8 * 8
+    # short chunks add fp32 K-split parts of grad_h (regions 256-byte aligned):
+    # 2048-row chunks of H = 4096 have 128 tiles -> 2 parts of 2048 x 4096
+    rup = lambda x: (x + 255) // 256 * 256
+    assert f(8192, 4096, 128256, 2048, BF16) == \
+        rup(rup(2048 * 128256 * 2) + 2048 * 1002 * 8) + 2 * 2048 * 4096 * 4
     # otherwise fp32 logits of one chunk
     assert f(100, 8, 5, 1000, BF16) == 100 * 5 * 4          # chunk clamped to N
     assert f(300, 136, 1000, 100, BF16) == 100 * 1000 * 4     # H % 64 != 0

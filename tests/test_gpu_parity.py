@@ -131,6 +131,9 @@ TINY = [
     (512, 256, 768, 256, "bf16"),    # all three contractions on that kernel
     (64, 64, 40000, 64, "bf16"),     # 313 half tiles per row
     (200, 128, 1000, 1000, "bf16"),  # one 200-row chunk (not a multiple of 8)
+    # few grad_h tiles: its K = V contraction is split in parts and summed
+    (512, 256, 4096, 512, "bf16"),   # 2 tiles -> 4 parts of 16 slabs
+    (1024, 512, 8192, 384, "bf16"),  # ragged 384/384/256-row chunks, 4 parts
     (3, 8, 5, 2, "f32"),
     (17, 24, 1000, 7, "f32"),
     (100, 64, 333, 33, "f32"),
@@ -282,8 +285,10 @@ def test_no_hidden_allocation(flce):
     gh = torch.empty_like(h)
     gw = torch.empty((V, H), dtype=torch.float32, device="cuda")
     need = flce.workspace_bytes(N, H, V, C, torch.bfloat16)
-    # bf16 exponentiated logits of one chunk + (max, sum) per 128-column half tile
-    assert need == C * V * 2 + C * (V // 128 + (V % 128 > 0)) * 8
+    # bf16 exponentiated logits of one chunk + (max, sum) per 128-column half
+    # tile + fp32 K-split parts of grad_h (8 tiles of 256 x 256 -> 4 parts)
+    rup = lambda x: (x + 255) // 256 * 256
+    assert need == rup(rup(C * V * 2) + C * (V // 128 + (V % 128 > 0)) * 8) + 4 * C * H * 4
     assert need <= C * V * 4 < cfg.naive_logits_bytes
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
