@@ -217,6 +217,10 @@ __device__ __forceinline__ void mma(f32x16 (&acc)[4][4], const bf16x8 (&a)[4],
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
+// Epilogues that may run with a K split (plain fp32 stores of each part).
+template <int EPI>
+constexpr bool kSplitK = EPI == kStoreF32;
+
 template <bool A_KC, bool B_KC, int EPI, typename OutT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
@@ -252,10 +256,11 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
   const int tni = r / gsize;
   const int m0 = tmi * kBM, n0 = tni * kBN;
 
-  // K split: workgroup row blockIdx.y takes its own run of slabs and its own
-  // output slice.
+  // K split (fp32 part stores only): workgroup row blockIdx.y takes its own
+  // run of slabs and its own output slice.  Compiled out of the other
+  // epilogues, whose register budget has no room for it.
   int KT = g.K / kBK;
-  if (g.splits > 1) {
+  if (kSplitK<EPI> && g.splits > 1) {
     const int per = (KT + g.splits - 1) / g.splits;
     const int kt0 = (int)blockIdx.y * per;
     KT = min(per, KT - kt0);  // >= 1: checked on the host
@@ -542,6 +547,7 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
   const int tiles_n = (g.N + kBN - 1) / kBN;
   int gm = g.group_m > 0 ? g.group_m : 4;
   if (gm > tiles_m) gm = tiles_m;
+  if (g.splits > 1 && !kSplitK<EPI>) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_bf16_dma_kernel<A_KC, B_KC, EPI, OutT>),
                      dim3(tiles_m * tiles_n, g.splits > 1 ? g.splits : 1), dim3(256), 0, s, g,
                      gm);
