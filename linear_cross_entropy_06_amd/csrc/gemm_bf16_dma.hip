@@ -186,16 +186,45 @@ struct FragOperand {
     }
   }
 
-  __device__ __forceinline__ void read(const char* slab, int kk, bf16x8 (&f)[4]) const {
+  // Ring slot s sits at LDS byte s * kTileBytes (the five slots are
+  // declared in order), but ds_read's immediate offset holds 16 bits only.
+  // For slots at 64 KiB and 128 KiB, off_hi[b - 1] = off + b * 64 KiB is
+  // kept in registers, opaque to the compiler, and the read address is
+  // written as slot + (off_hi - b * 64 KiB): the constant parts cancel into
+  // the immediate, the slot object still names what is read (so loads into
+  // other slots are known not to interfere), and no address is recomputed
+  // inside the K loop.  Were the slots laid out otherwise, the addresses
+  // would still be exact, only computed with extra adds.
+  uint32_t off_hi[2][4];
+
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        off_hi[b][x] = off[x] + (uint32_t)(b + 1) * 65536u;
+        asm volatile("" : "+v"(off_hi[b][x]));
+      }
+  }
+
+  // Byte offset of piece x inside slot s (a compile-time index).
+  __device__ __forceinline__ int piece(int s, int x) const {
+    const int b = s * kTileBytes / 65536;
+    return b == 0 ? (int)off[x] : (int)off_hi[b - 1][x] - b * 65536;
+  }
+
+  // Fragments of k step kk from `slab`, ring slot s.
+  __device__ __forceinline__ void read(const char* slab, int s, int kk,
+                                       bf16x8 (&f)[4]) const {
     if constexpr (KC) {
-      const char* p = slab + off[kk];
+      const char* p = slab + piece(s, kk);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         f[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p + 4096 * i));
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const char* p = slab + off[i] + kk * 8192;
+        const char* p = slab + piece(s, i) + kk * 8192;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 2048));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
@@ -252,8 +281,11 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
   const int first_m = grp * gm;
   const int gsize = min(tiles_m - first_m, gm);
   const int r = t - grp * per_group;
-  const int tmi = first_m + r % gsize;
-  const int tni = r / gsize;
+  // The integer divisions run on the vector unit; readfirstlane states that
+  // the results are wave-uniform, so every address derived from them (the
+  // DMA buffer resources above all) stays in scalar registers.
+  const int tmi = __builtin_amdgcn_readfirstlane(first_m + r % gsize);
+  const int tni = __builtin_amdgcn_readfirstlane(r / gsize);
   const int m0 = tmi * kBM, n0 = tni * kBN;
 
   // K split (fp32 part stores only): workgroup row blockIdx.y takes its own
@@ -278,6 +310,8 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
   FragOperand<B_KC> fb;
   fa.init(wm * 128, lane);
   fb.init(wn * 128, lane);
+  fa.pin();
+  fb.pin();
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -288,7 +322,8 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   da.kt_total = db.kt_total = KT;
-  da.start = db.start = g.stagger > 0 ? (int)(((unsigned)grp * (unsigned)g.stagger) % (unsigned)KT) : 0;
+  da.start = db.start = __builtin_amdgcn_readfirstlane(
+      g.stagger > 0 ? (int)(((unsigned)grp * (unsigned)g.stagger) % (unsigned)KT) : 0);
   // Prologue: A_0 -> slot 0, B_0 -> slot 1, A_1 -> slot 2; wait for the
   // first two (the A_1 requests, issued last, may still be in flight).
   da.issue(0, slots[0], wave);
@@ -298,8 +333,8 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
   block_barrier();
 
   bf16x8 a0[4], b0[4], a1[4], b1[4];
-  fa.read(slots[0], 0, a0);
-  fb.read(slots[1], 0, b0);
+  fa.read(slots[0], 0, 0, a0);
+  fb.read(slots[1], 1, 0, b0);
 
   // LDS fragment reads per k step (ds_read_b128 per 32-row block, or two
   // ds_read_b64_tr_b16 for m-contiguous operands).
@@ -310,20 +345,20 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
   // reads finished before the barrier that ended slab kt-1.  Requests past
   // the last slab re-fetch the last slab (L2 hits, never read) so the body
   // stays one basic block.
-  auto slab_step = [&](int kt, char* sa, char* sb, char* sa1, char* sb1, char* sa2)
+  auto slab_step = [&](int kt, int sa, int sb, int sa1, int sb1, int sa2)
       __attribute__((always_inline)) {
     const int kn1 = kt + 1 < KT ? kt + 1 : KT - 1;
     const int kn2 = kt + 2 < KT ? kt + 2 : KT - 1;
-    fa.read(sa, 1, a1);
-    fb.read(sb, 1, b1);
-    db.issue(kn1, sb1, wave);
-    da.issue(kn2, sa2, wave);
+    fa.read(slots[sa], sa, 1, a1);
+    fb.read(slots[sb], sb, 1, b1);
+    db.issue(kn1, slots[sb1], wave);
+    da.issue(kn2, slots[sa2], wave);
     mma<0, 4>(acc, a0, b0);
-    fa.read(sa, 2, a0);
-    fb.read(sb, 2, b0);
+    fa.read(slots[sa], sa, 2, a0);
+    fb.read(slots[sb], sb, 2, b0);
     mma<0, 4>(acc, a1, b1);
-    fa.read(sa, 3, a1);
-    fb.read(sb, 3, b1);
+    fa.read(slots[sa], sa, 3, a1);
+    fb.read(slots[sb], sb, 3, b1);
     mma<0, 4>(acc, a0, b0);
     mma<0, 2>(acc, a1, b1);
     // Issue order: each k step requests the fragments of the next step
@@ -357,17 +392,16 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
     wait_lgkmcnt0();
     block_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    fa.read(sa1, 0, a0);
-    fb.read(sb1, 0, b0);
+    fa.read(slots[sa1], sa1, 0, a0);
+    fb.read(slots[sb1], sb1, 0, b0);
     mma<2, 4>(acc, a1, b1);
     __builtin_amdgcn_sched_group_barrier(0x100, kReads, 1);
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
   };
   // Slab kt with p = kt mod 5.
   auto step = [&](int kt, int p) __attribute__((always_inline)) {
-    slab_step(kt, slots[(2 * p) % kSlots], slots[(2 * p + 1) % kSlots],
-              slots[(2 * p + 2) % kSlots], slots[(2 * p + 3) % kSlots],
-              slots[(2 * p + 4) % kSlots]);
+    slab_step(kt, (2 * p) % kSlots, (2 * p + 1) % kSlots, (2 * p + 2) % kSlots,
+              (2 * p + 3) % kSlots, (2 * p + 4) % kSlots);
   };
   int kt = 0;
   for (; kt + kSlots <= KT; kt += kSlots) {
@@ -384,30 +418,15 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
   // The last slab's look-ahead requests must land before the workgroup's
   // LDS can be handed to another workgroup.
   wait_vmcnt<0>();
+  // The epilogue works from an opaque copy of the lane index, so none of its
+  // address arithmetic is hoisted above the K loop, where it would hold
+  // registers the loop needs.
+  int lane_ep = lane;
+  asm volatile("" : "+v"(lane_ep));
 
   // Epilogue.  Accumulator r of lane l in block (i, j) is
   // D[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32] of that 32x32 block.
-  if constexpr (EPI == kStoreOut && sizeof(OutT) == 2) {
-    // bf16 output (one launch of long K per tile: the epilogue is a small
-    // share of the tile's time): stored straight from the accumulators.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 128 + j * 32 + (lane & 31);
-        if (n >= g.N) continue;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m = m0 + wm * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
-          if (m >= g.M) continue;  // M % 8 == 0: a run of 4 is all in or all out
-          u32x2 w;
-          w[0] = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-          w[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + (int64_t)n * g.ldo + m) = w;
-        }
-      }
-    }
-  } else {
+  {
     // Each lane holds 16-byte pieces of 32 different output rows, so direct
     // stores would send 32 partial-line requests per instruction.  Each wave
     // instead transposes its results a block at a time through its own
@@ -417,125 +436,172 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
     // accumulating, every load of the previous value) covers whole lines.
     // All look-ahead DMA requests of every wave have landed once all waves
     // pass this barrier; the operand ring is free.
+    const int lane = lane_ep;
     block_barrier();
     char* const buf = wave == 0 ? slot0 : wave == 1 ? slot1 : wave == 2 ? slot2 : slot3;
     const int c_rd = lane & 7;  // 16-byte chunk this lane reads back
     auto lds_off = [](int nl, int c) { return nl * 128 + ((c ^ ((nl >> 1) & 7)) << 4); };
-    if constexpr (EPI == kExpBF16) {
-      // Exponentiated logits in bf16 (32(m) x 128(n) blocks i = 2p, 2p+1
-      // fill one 128-byte row segment of m), and per column and half tile
-      // the (max, sum) pair.  Lanes l and l ^ 32 hold the two halves of
-      // every 32-row block, so one shuffle completes a column over the
-      // wave's 128 rows.
-      // Tiles wholly inside the output skip every per-element edge test.
-      auto exp_body = [&](auto guard_tag) __attribute__((always_inline)) {
+    if constexpr (EPI == kExpBF16 || (EPI == kStoreOut && sizeof(OutT) == 2)) {
+      // bf16 output, 32(m) x 128(n) blocks i = 2p, 2p+1 filling one
+      // 128-byte row segment of m per row n; addresses are 32-bit offsets
+      // from the wave's corner of the output (ldo < 2^22).  For the
+      // exponentiated logits the values are 2^(z log2 e - mx) with mx the
+      // column maximum over each 128-row half tile, and the (max, sum) pair
+      // of every column and half tile is written too: lanes l and l ^ 32
+      // hold the two halves of every 32-row block, so one shuffle completes
+      // a column over the wave's 128 rows.  Tiles wholly inside the output
+      // skip every per-element edge test.
+      constexpr bool kExp = EPI == kExpBF16;
+      auto bf16_body = [&](auto guard_tag) __attribute__((always_inline)) {
         constexpr bool kGuard = decltype(guard_tag)::value;
         constexpr float kL2e = 1.4426950408889634f;
         const int hl = lane >> 5;
+        uint16_t* const corner = static_cast<uint16_t*>(g.out) +
+                                 ((int64_t)(n0 + wn * 128) * g.ldo + (m0 + wm * 128));
+        const uint32_t row8 = 8u * (uint32_t)g.ldo;
+        const uint32_t lane_off = (uint32_t)(lane >> 3) * (uint32_t)g.ldo + 8u * c_rd;
+        const int n_lane = n0 + wn * 128 + (lane >> 3);
         float mneg[4], ssum[4];
-  #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float mz = -__builtin_inff();
-  #pragma unroll
-          for (int i = 0; i < 4; ++i)
-  #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (!kGuard || m0 + wm * 128 + i * 32 + 8 * q + 4 * hl < g.M)
-  #pragma unroll
-                for (int e = 0; e < 4; ++e) mz = fmaxf(mz, acc[i][j][4 * q + e]);
-          mz = fmaxf(mz, __shfl_xor(mz, 32, 64));
-          // No row of this half tile below M: nothing is stored for it.
-          mneg[j] = mz == -__builtin_inff() ? 0.0f : -to_log2(mz);
-          ssum[j] = 0.0f;
+        if constexpr (kExp) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float mz = -__builtin_inff();
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (!kGuard || m0 + wm * 128 + i * 32 + 8 * q + 4 * hl < g.M)
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) mz = fmaxf(mz, acc[i][j][4 * q + e]);
+            mz = fmaxf(mz, __shfl_xor(mz, 32, 64));
+            // No row of this half tile below M: nothing is stored for it.
+            mneg[j] = mz == -__builtin_inff() ? 0.0f : -to_log2(mz);
+            ssum[j] = 0.0f;
+          }
         }
-  #pragma unroll
+#pragma unroll
         for (int p = 0; p < 2; ++p) {
-  #pragma unroll
+#pragma unroll
           for (int ii = 0; ii < 2; ++ii) {
             const int i = 2 * p + ii;
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int nl = 32 * j + (lane & 31);
-  #pragma unroll
+#pragma unroll
               for (int q = 0; q < 4; ++q) {
-                const bool ok = !kGuard || m0 + wm * 128 + i * 32 + 8 * q + 4 * hl < g.M;
                 float u[4];
-  #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  u[e] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][4 * q + e], kL2e,
-                                                                     mneg[j]))
-                            : 0.0f;
-                ssum[j] += (u[0] + u[1]) + (u[2] + u[3]);
+                if constexpr (kExp) {
+                  const bool ok = !kGuard || m0 + wm * 128 + i * 32 + 8 * q + 4 * hl < g.M;
+#pragma unroll
+                  for (int e = 0; e < 4; ++e)
+                    u[e] = ok ? __builtin_amdgcn_exp2f(
+                                    __builtin_fmaf(acc[i][j][4 * q + e], kL2e, mneg[j]))
+                              : 0.0f;
+                  ssum[j] += (u[0] + u[1]) + (u[2] + u[3]);
+                } else {
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) u[e] = acc[i][j][4 * q + e];
+                }
                 const u32x2 w = {pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3])};
                 *reinterpret_cast<u32x2*>(buf + lds_off(nl, 4 * ii + q) + 8 * hl) = w;
               }
             }
           }
-          const int m = m0 + wm * 128 + 64 * p + 8 * c_rd;
-  #pragma unroll
+          const bool m_ok = !kGuard || m0 + wm * 128 + 64 * p + 8 * c_rd < g.M;
+#pragma unroll
           for (int t = 0; t < 16; ++t) {
             const int nl = 8 * t + (lane >> 3);
             const u32x4 v = *reinterpret_cast<const u32x4*>(buf + lds_off(nl, c_rd));
-            const int n = n0 + wn * 128 + nl;
-            if (!kGuard || (n < g.N && m < g.M))  // M % 8 == 0: runs of 8 all in or out
-              *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.out) + (int64_t)n * g.ldo + m) = v;
+            // M % 8 == 0: a run of 8 is all in or all out
+            if (!kGuard || (m_ok && n_lane + 8 * t < g.N))
+              *reinterpret_cast<u32x4*>(corner + (lane_off + (uint32_t)t * row8 + 64u * p)) = v;
           }
         }
-  #pragma unroll
-        for (int j = 0; j < 4; ++j) ssum[j] += __shfl_xor(ssum[j], 32, 64);
-        if (lane < 32 && m0 + wm * 128 < g.M) {
-  #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = n0 + wn * 128 + 32 * j + lane;
-            if (!kGuard || n < g.N) {
-              float* pr = g.row_part + (int64_t)n * g.ldp + 2 * (2 * tmi + wm);
-              pr[0] = -mneg[j];
-              pr[1] = ssum[j];
+        if constexpr (kExp) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ssum[j] += __shfl_xor(ssum[j], 32, 64);
+          if (lane < 32 && m0 + wm * 128 < g.M) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int n = n0 + wn * 128 + 32 * j + lane;
+              if (!kGuard || n < g.N) {
+                float* pr = g.row_part + (int64_t)n * g.ldp + 2 * (2 * tmi + wm);
+                pr[0] = -mneg[j];
+                pr[1] = ssum[j];
+              }
             }
           }
         }
       };
       if (m0 + kBM <= g.M && n0 + kBN <= g.N)
-        exp_body(std::integral_constant<bool, false>{});
+        bf16_body(std::integral_constant<bool, false>{});
       else
-        exp_body(std::integral_constant<bool, true>{});
+        bf16_body(std::integral_constant<bool, true>{});
     } else {
       // fp32 output: one 32(m) x 128(n) block i at a time, double-buffered.
-      const bool accumulate = EPI == kAccumF32 && g.beta;
+      // Addresses are 32-bit offsets from the wave's corner of the output
+      // (its 128 x 128 block spans < 2^32 bytes: ldo < 2^22 floats).  The
+      // accumulate and edge decisions are made once per tile, so a full
+      // tile's stores carry no branches; without accumulation no memory
+      // read is pending and the stores stream with no waits, and with it
+      // each block's 16 previous values are fetched in one batch (loads and
+      // stores share one completion counter, so a later wait drains both).
+      auto f32_body = [&](auto guard_tag, auto acc_tag) __attribute__((always_inline)) {
+        constexpr bool kGuard = decltype(guard_tag)::value;
+        constexpr bool kAcc = decltype(acc_tag)::value;
+        float* const corner = static_cast<float*>(g.out) +
+                              ((int64_t)(n0 + wn * 128) * g.ldo + (m0 + wm * 128));
+        const uint32_t row8 = 8u * (uint32_t)g.ldo;
+        const uint32_t lane_off = (uint32_t)(lane >> 3) * (uint32_t)g.ldo + 4u * c_rd;
+        const int n_lane = n0 + wn * 128 + (lane >> 3);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        char* const b = buf + (i & 1) * 16384;
-        const int m = m0 + wm * 128 + i * 32 + 4 * c_rd;
-        f32x4 old[16];
-        if (accumulate) {
+        for (int i = 0; i < 4; ++i) {
+          char* const b = buf + (i & 1) * 16384;
+          const int m = m0 + wm * 128 + i * 32 + 4 * c_rd;
+          const bool m_ok = !kGuard || m < g.M;
+          f32x4 old[16];
+          if constexpr (kAcc) {
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+              const float* src = corner + (lane_off + (uint32_t)t * row8 + 32u * i);
+              if (!kGuard || (m_ok && n_lane + 8 * t < g.N))
+                old[t] = *reinterpret_cast<const f32x4*>(src);
+              else
+                old[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int nl = 32 * j + (lane & 31);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                               acc[i][j][4 * q + 3]};
+              *reinterpret_cast<f32x4*>(b + lds_off(nl, 2 * q + (lane >> 5))) = v;
+            }
+          }
 #pragma unroll
           for (int t = 0; t < 16; ++t) {
-            const int n = n0 + wn * 128 + 8 * t + (lane >> 3);
-            if (n < g.N && m < g.M)
-              old[t] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(g.out) +
-                                                       (int64_t)n * g.ldo + m);
+            const int nl = 8 * t + (lane >> 3);
+            f32x4 v = *reinterpret_cast<const f32x4*>(b + lds_off(nl, c_rd));
+            if constexpr (kAcc) v += old[t];
+            float* dst = corner + (lane_off + (uint32_t)t * row8 + 32u * i);
+            if (!kGuard || (m_ok && n_lane + 8 * t < g.N))
+              *reinterpret_cast<f32x4*>(dst) = v;
           }
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int nl = 32 * j + (lane & 31);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                             acc[i][j][4 * q + 3]};
-            *reinterpret_cast<f32x4*>(b + lds_off(nl, 2 * q + (lane >> 5))) = v;
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int nl = 8 * t + (lane >> 3);
-          f32x4 v = *reinterpret_cast<const f32x4*>(b + lds_off(nl, c_rd));
-          const int n = n0 + wn * 128 + nl;
-          if (n < g.N && m < g.M) {
-            if (accumulate) v += old[t];
-            *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + (int64_t)n * g.ldo + m) = v;
-          }
-        }
+      };
+      const bool full = m0 + kBM <= g.M && n0 + kBN <= g.N;
+      if (EPI == kAccumF32 && g.beta) {
+        if (full)
+          f32_body(std::integral_constant<bool, false>{}, std::integral_constant<bool, true>{});
+        else
+          f32_body(std::integral_constant<bool, true>{}, std::integral_constant<bool, true>{});
+      } else {
+        if (full)
+          f32_body(std::integral_constant<bool, false>{}, std::integral_constant<bool, false>{});
+        else
+          f32_body(std::integral_constant<bool, true>{}, std::integral_constant<bool, false>{});
       }
     }
   }
@@ -565,6 +631,8 @@ bool gemm_bf16_dma_supported(bool a_kc, bool b_kc, const GemmArgs& g) {
   // Operand pieces are addressed by 32-bit offsets within 256 rows (k-
   // contiguous) or 64 k-rows (m-contiguous) of a leading dimension.
   if (g.lda >= (int64_t{1} << 22) || g.ldb >= (int64_t{1} << 22)) return false;
+  // fp32 epilogue offsets within a wave's 128 output rows are 32-bit.
+  if (g.ldo >= (int64_t{1} << 22)) return false;
   if (g.splits > 1) {  // every part gets at least one slab
     const int kt = g.K / kBK, per = (kt + g.splits - 1) / g.splits;
     if ((g.splits - 1) * per >= kt || g.splits > 65535) return false;
