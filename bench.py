@@ -52,9 +52,12 @@ def parse_args():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=4096)
-    p.add_argument("--op", choices=("flce", "ce"), default="flce",
+    p.add_argument("--op", choices=("flce", "ce", "vocab"), default="flce",
                    help="flce: the fused head (default); ce: cross entropy on given bf16 "
-                        "logits [1024, 128256] (flce_cross_entropy)")
+                        "logits [1024, 128256] (flce_cross_entropy); vocab: the fused head "
+                        "through flce_fwd_bwd_vocab (vocabulary chunks)")
+    p.add_argument("--vchunk", type=int, default=16384,
+                   help="vocabulary chunk of --op vocab")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="first run one elementwise fp32 copy of this many MiB (a kernel of "
                         "known traffic, used to scale FETCH_SIZE/WRITE_SIZE counters)")
@@ -188,13 +191,102 @@ def bench_ce(args) -> int:
     return 0
 
 
+def bench_vocab(args) -> int:
+    """The fused head through flce_fwd_bwd_vocab on a workload (all tokens at
+    once, the vocabulary in chunks of --vchunk columns; the logits are formed
+    twice, 8 N V H flops, of which 6 N V H are the head's own)."""
+    import numpy as np
+    import torch
+
+    import linear_cross_entropy_06_amd as flce
+    from synth import config_by_name, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    flce.load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg = config_by_name(args.workload)
+    inp = make_inputs(cfg, seed=args.seed)
+    h, W, t = inp.h.to(dev), inp.W.to(dev), inp.t.to(dev)
+    N, H, V, vc = cfg.N, cfg.H, cfg.V, args.vchunk
+    need = flce.vocab_workspace_bytes(N, H, V, vc, h.dtype)
+    if need == 0:
+        print(f"bench.py: {cfg.name} with vchunk {vc} is not a shape flce_fwd_bwd_vocab runs",
+              file=sys.stderr)
+        return 1
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    gh = torch.empty_like(h)
+    gw = torch.empty((V, H), dtype=torch.float32, device=dev)
+    kw = dict(loss=loss, grad_h=gh, grad_W=gw, workspace=ws)
+    for _ in range(max(1, args.warmup)):
+        flce.fwd_bwd_vocab(h, W, t, vc, **kw)
+    torch.cuda.synchronize()
+    loss0 = float(loss)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        flce.fwd_bwd_vocab(h, W, t, vc, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    head_flops = 6.0 * N * V * H
+    run_flops = 8.0 * N * V * H
+    out = {
+        "metric": "FLCE fwd+bwd tokens/s (vocabulary-chunked entry point)",
+        "value": N / (ms * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": cfg.name, "N": N, "H": H, "V": V, "vchunk": vc,
+                   "seed": args.seed},
+        "head_tflops": head_flops / (ms * 1e-3) / 1e12,
+        "executed_tflops": run_flops / (ms * 1e-3) / 1e12,
+        "workspace_bytes": need,
+        "naive_logits_bytes": N * V * 4,
+        "token_chunk_workspace_bytes_c4096": flce.workspace_bytes(N, H, V, 4096, h.dtype),
+        "loss": loss0,
+        "roofline": {
+            "kernel": "fwd_bwd_vocab (all launches of one call)", "bound": "mfma",
+            "achieved": run_flops / (ev_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": run_flops / (ev_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "traffic": None, "work_per_launch": f"8*{N}*{V}*{H} = {run_flops:.4e} flop",
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from synth import to_float64
+        S = 2048
+        hh = to_float64(inp.h[:S])
+        WW = to_float64(inp.W)
+        tt = inp.t[:S].numpy().astype(np.int64)
+        c0 = time.perf_counter()
+        oracle.flce_vocab_chunked(hh, WW, tt, vc)
+        dt = time.perf_counter() - c0
+        out["cpu_baseline"] = {
+            "value": S / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"first {S} of {N} tokens against the full {V}x{H} head, fp64 numpy "
+                      f"flce_vocab_chunked (vchunk {vc}): {dt:.2f} s"}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
-    if args.op == "ce":
+    if args.op in ("ce", "vocab"):
         if args.gpus != 1:
             print("bench.py: this build runs on one GPU only", file=sys.stderr)
             return 2
-        return bench_ce(args)
+        return bench_ce(args) if args.op == "ce" else bench_vocab(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "

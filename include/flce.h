@@ -55,7 +55,8 @@ typedef enum flce_status {
   FLCE_OK = 0,
   FLCE_ERR_INVALID_ARG = 1, /* null pointer, size < 1 or >= 2^31, bad dtype */
   FLCE_ERR_WORKSPACE = 2,   /* workspace smaller than flce_workspace_bytes   */
-  FLCE_ERR_UNSUPPORTED = 3, /* H % 8 != 0 or a pointer not 16-byte aligned   */
+  FLCE_ERR_UNSUPPORTED = 3, /* H % 8 != 0, a pointer not 16-byte aligned,
+                               or a shape the entry point does not run    */
   FLCE_ERR_HIP = 4          /* the HIP runtime reported a launch error       */
 } flce_status;
 
@@ -207,6 +208,46 @@ flce_status flce_ce_rows(float* z, int64_t ldz, const int32_t* targets,
 flce_status flce_cross_entropy(void* logits, int64_t ld, const int32_t* targets,
                                int64_t rows, int64_t V, float* loss, float* row_loss,
                                flce_dtype dt, hipStream_t stream);
+
+/*
+ * Vocabulary-chunked variant of flce_fwd_bwd (page 1, "Liger Kernel
+ * explained", section "What does Liger Kernel actually fuse, and why does
+ * that cut memory?": the logits are worked through in chunks over the
+ * vocabulary dimension), for few tokens and a large vocabulary, where token
+ * chunks would be short.  All N tokens are processed together and the
+ * vocabulary in column chunks of Vc = min(vchunk, V):
+ *   pass 1  the logits of every column chunk are formed only for their
+ *           per-row (max, sum of exponentials) statistics, which give every
+ *           row's log-sum-exp and loss;
+ *   pass 2  each chunk's logits are formed again and become
+ *           G = (softmax - onehot) / N with the global log-sum-exp; then
+ *           grad_h += G W_c (fp32 accumulator in the workspace) and
+ *           grad_W[chunk rows] = G^T h.
+ * The logits are computed twice (8 N V H flops instead of 6 N V H).  The
+ * arguments, outputs and rules are those of flce_fwd_bwd with `vchunk` in
+ * place of `chunk`; loss, grad_h and grad_W are overwritten.
+ * Supported: FLCE_BF16, H % 64 == 0, V % 64 == 0, vchunk >= V or
+ * vchunk % 128 == 0, H and V below 2^22; otherwise FLCE_ERR_UNSUPPORTED
+ * (flce_fwd_bwd covers every shape).
+ */
+flce_status flce_fwd_bwd_vocab(const void* h, const void* W, const int32_t* targets,
+                               int64_t N, int64_t H, int64_t V, int64_t vchunk,
+                               float* loss, void* grad_h, float* grad_W,
+                               void* workspace, size_t workspace_bytes,
+                               flce_dtype dt, hipStream_t stream);
+
+/*
+ * Bytes of device workspace flce_fwd_bwd_vocab needs, with Vc = min(vchunk,
+ * V), each region rounded up to 256 bytes:
+ *   N * Vc * 2            bf16 logits of one vocabulary chunk
+ * + N * ceil(V/128) * 8   (max, sum) per row and 128-column slice
+ * + N * 12                per-row log-sum-exp, target logit and loss
+ * + N * H * 4             fp32 grad_h accumulator
+ * Returns 0 when a size is < 1 or the shape is not supported by this entry
+ * point.  Pure host function.
+ */
+size_t flce_vocab_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t vchunk,
+                                  flce_dtype dt);
 
 /* A static, human-readable name for a status code (host only). */
 const char* flce_status_string(flce_status s);

@@ -19,11 +19,13 @@ from ._lib import (
     cross_entropy,
     cross_entropy_,
     fwd_bwd,
+    fwd_bwd_vocab,
     launch_count,
     linear_cross_entropy,
     load,
     logits,
     scale_grads,
+    vocab_workspace_bytes,
     workspace_bytes,
 )
 
@@ -42,10 +44,12 @@ __all__ = [
     "cross_entropy",
     "cross_entropy_",
     "fwd_bwd",
+    "fwd_bwd_vocab",
     "launch_count",
     "linear_cross_entropy",
     "load",
     "logits",
     "scale_grads",
+    "vocab_workspace_bytes",
     "workspace_bytes",
 ]

@@ -40,6 +40,8 @@ EXPORTS = (
     "flce_logits",
     "flce_ce_rows",
     "flce_cross_entropy",
+    "flce_fwd_bwd_vocab",
+    "flce_vocab_workspace_bytes",
     "flce_status_string",
 )
 
@@ -87,6 +89,10 @@ def load() -> ctypes.CDLL:
     lib.flce_ce_rows.restype = ctypes.c_int
     lib.flce_cross_entropy.argtypes = [vp, i64, vp, i64, i64, vp, vp, ctypes.c_int, vp]
     lib.flce_cross_entropy.restype = ctypes.c_int
+    lib.flce_fwd_bwd_vocab.argtypes = lib.flce_fwd_bwd.argtypes
+    lib.flce_fwd_bwd_vocab.restype = ctypes.c_int
+    lib.flce_vocab_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.flce_vocab_workspace_bytes.restype = sz
     lib.flce_status_string.argtypes = [ctypes.c_int]
     lib.flce_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -212,6 +218,51 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
         st = lib.flce_fwd_bwd(*args)
     else:
         st = lib.flce_fwd_bwd_timed(*args, events.array, events.n)
+    _check(st)
+    return loss, grad_h, grad_W
+
+
+def vocab_workspace_bytes(N: int, H: int, V: int, vchunk: int, dtype: torch.dtype) -> int:
+    """Workspace of ``flce_fwd_bwd_vocab`` (0: shape not supported there)."""
+    dt = FLCE_BF16 if dtype == torch.bfloat16 else FLCE_F32
+    return int(load().flce_vocab_workspace_bytes(N, H, V, vchunk, dt))
+
+
+def fwd_bwd_vocab(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, vchunk: int, *,
+                  loss: Optional[torch.Tensor] = None,
+                  grad_h: Optional[torch.Tensor] = None,
+                  grad_W: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None,
+                  ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """The same outputs as ``fwd_bwd`` through ``flce_fwd_bwd_vocab``: all
+    tokens at once, the vocabulary in column chunks of ``vchunk`` (logits
+    formed twice; bf16 with H % 64 == 0, V % 64 == 0 and vchunk % 128 == 0
+    or vchunk >= V)."""
+    lib = load()
+    _need_cuda(h, W, targets)
+    if targets.dtype != torch.int32:
+        raise TypeError("targets must be int32")
+    if W.dtype != h.dtype:
+        raise TypeError("h and W must share a dtype")
+    N, H = h.shape
+    V = W.shape[0]
+    dt = _dt(h)
+    dev = h.device
+    if loss is None:
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+    if grad_h is None:
+        grad_h = torch.empty_like(h)
+    if grad_W is None:
+        grad_W = torch.empty((V, H), dtype=torch.float32, device=dev)
+    need = int(lib.flce_vocab_workspace_bytes(N, H, V, int(vchunk), dt))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need_cuda(loss, grad_h, grad_W, workspace)
+    st = lib.flce_fwd_bwd_vocab(h.data_ptr(), W.data_ptr(), targets.data_ptr(), N, H, V,
+                                int(vchunk), loss.data_ptr(), grad_h.data_ptr(),
+                                grad_W.data_ptr(), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), dt,
+                                _stream_ptr(dev))
     _check(st)
     return loss, grad_h, grad_W
 

@@ -31,6 +31,12 @@
 //
 // The exponentials run in base 2 on the hardware v_exp_f32 / v_log_f32.
 //
+// ce_stats_exp / ce_rewrite_exp (vocabulary chunks): the same two halves
+// split in time, for a path that walks the vocabulary in column chunks:
+// after every chunk's pairs exist, lse2_i, log2 z[i, t_i] and the row loss;
+// then, chunk by chunk, G over that chunk's columns, with the target's
+// element rewritten when it falls in the chunk.
+//
 // loss_sum: the per-row losses of a chunk, summed in fp64 in a fixed order
 // (deterministic), scaled and added to the running fp32 loss.
 #include "flce_internal.h"
@@ -208,21 +214,8 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int UNROLL>
-__global__ void __launch_bounds__(64 * kWavesPerBlock)
-ce_rows_exp_kernel(uint16_t* __restrict__ u, int64_t ldu, const float* __restrict__ row_part,
-                   int64_t ldp, const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
-                   int H, const int32_t* __restrict__ targets, int rows, int V, float scale,
-                   float* __restrict__ row_loss, int64_t loss_stride) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int t = targets[row];
-  const bool t_ok = (t >= 0) && (t < V);
-
-  // lse2 from the (max, sum) pairs of the row's half tiles.
-  const float* pr = row_part + (int64_t)row * ldp;
-  const int nq = (V + kHalfTile - 1) / kHalfTile;
+// lse2 of a row from its nq (max, sum) pairs (one wave; every lane gets it).
+__device__ __forceinline__ float lse2_from_pairs(const float* pr, int nq, int lane) {
   float m = -INFINITY, s = 0.0f;
   for (int q = lane; q < nq; q += 64) combine(m, s, pr[2 * q], pr[2 * q + 1]);
 #pragma unroll
@@ -231,33 +224,35 @@ ce_rows_exp_kernel(uint16_t* __restrict__ u, int64_t ldu, const float* __restric
     const float s2 = __shfl_xor(s, off, 64);
     combine(m, s, m2, s2);
   }
-  const float lse2 = m + log2_hw(s);
+  return m + log2_hw(s);
+}
 
-  // Target logit z_t = h_row . W_t (an out-of-range target is never
-  // dereferenced: the loss becomes NaN).
-  float zt = __builtin_nanf("");
-  if (t_ok) {
-    const u32x4* hv = reinterpret_cast<const u32x4*>(h + (int64_t)row * H);
-    const u32x4* wv = reinterpret_cast<const u32x4*>(W + (int64_t)t * H);
-    float acc = 0.0f;
-    for (int k = lane; k < H / 8; k += 64) {
-      const u32x4 a = hv[k], b = wv[k];
+// Target logit z_t = h_row . W_t (bf16 rows, fp32 accumulation; every lane
+// gets it).
+__device__ __forceinline__ float target_logit(const uint16_t* h_row, const uint16_t* w_row, int H,
+                                              int lane) {
+  const u32x4* hv = reinterpret_cast<const u32x4*>(h_row);
+  const u32x4* wv = reinterpret_cast<const u32x4*>(w_row);
+  float acc = 0.0f;
+  for (int k = lane; k < H / 8; k += 64) {
+    const u32x4 a = hv[k], b = wv[k];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc += bf16_lo(a[e]) * bf16_lo(b[e]) + bf16_hi(a[e]) * bf16_hi(b[e]);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    zt = acc;
+    for (int e = 0; e < 4; ++e)
+      acc += bf16_lo(a[e]) * bf16_lo(b[e]) + bf16_hi(a[e]) * bf16_hi(b[e]);
   }
-  if (lane == 0) row_loss[(int64_t)row * loss_stride] = (lse2 - to_log2(zt)) * kLn2;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  return acc;
+}
 
-  // G = u * 2^(mx_q - lse2) * scale, in place, 8 elements (one half-tile
-  // slice) per lane and step.
-  const float shift = lse2 - log2_hw(scale);
-  uint16_t* ur = u + (int64_t)row * ldu;
+// u -> u * 2^(mx_q - shift) over n elements of a row (n % 8 == 0), in
+// place, 8 elements (one slice of a half tile) per lane and step; pr holds
+// the row's (max, sum) pairs from the row's first element on.
+template <int UNROLL>
+__device__ __forceinline__ void rescale_row(uint16_t* ur, const float* pr, int n, float shift,
+                                            int lane) {
   u32x4* uv = reinterpret_cast<u32x4*>(ur);
-  const int nvec = V >> 3;
+  const int nvec = n >> 3;
   for (int v0 = 0; v0 < nvec; v0 += 64 * UNROLL) {
     u32x4 x[UNROLL];
     float f[UNROLL];
@@ -280,11 +275,86 @@ ce_rows_exp_kernel(uint16_t* __restrict__ u, int64_t ldu, const float* __restric
       __builtin_nontemporal_store(w, &uv[v]);
     }
   }
+}
+
+template <int UNROLL>
+__global__ void __launch_bounds__(64 * kWavesPerBlock)
+ce_rows_exp_kernel(uint16_t* __restrict__ u, int64_t ldu, const float* __restrict__ row_part,
+                   int64_t ldp, const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+                   int H, const int32_t* __restrict__ targets, int rows, int V, float scale,
+                   float* __restrict__ row_loss, int64_t loss_stride) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int t = targets[row];
+  const bool t_ok = (t >= 0) && (t < V);
+
+  // lse2 from the (max, sum) pairs of the row's half tiles.
+  const float* pr = row_part + (int64_t)row * ldp;
+  const float lse2 = lse2_from_pairs(pr, (V + kHalfTile - 1) / kHalfTile, lane);
+
+  // Target logit (an out-of-range target is never dereferenced: the loss
+  // becomes NaN).
+  const float zt =
+      t_ok ? target_logit(h + (int64_t)row * H, W + (int64_t)t * H, H, lane) : __builtin_nanf("");
+  if (lane == 0) row_loss[(int64_t)row * loss_stride] = (lse2 - to_log2(zt)) * kLn2;
+
+  // G = u * 2^(mx_q - lse2) * scale, in place.
+  uint16_t* ur = u + (int64_t)row * ldu;
+  rescale_row<UNROLL>(ur, pr, V, lse2 - log2_hw(scale), lane);
   if (t_ok && lane == 0) {
     // After this wave's stores of the row have completed (the target's
     // element among them), overwrite that element.
     __builtin_amdgcn_s_waitcnt(0);
     const float pt = exp2_hw(to_log2(zt) - lse2);
+    ur[t] = (uint16_t)bf16_bits((pt - 1.0f) * scale);
+  }
+}
+
+// Vocabulary-chunked statistics: after the exponentiated logits of every
+// vocabulary chunk have left their (max, sum) pairs, per row lse2 (all V
+// columns), log2 of the target logit, and the row loss.
+__global__ void __launch_bounds__(64 * kWavesPerBlock)
+ce_stats_exp_kernel(const float* __restrict__ row_part, int64_t ldp,
+                    const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int H,
+                    const int32_t* __restrict__ targets, int rows, int V,
+                    float* __restrict__ lse2_out, float* __restrict__ zt2_out,
+                    float* __restrict__ row_loss) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int t = targets[row];
+  const bool t_ok = (t >= 0) && (t < V);
+  const float lse2 =
+      lse2_from_pairs(row_part + (int64_t)row * ldp, (V + kHalfTile - 1) / kHalfTile, lane);
+  const float zt =
+      t_ok ? target_logit(h + (int64_t)row * H, W + (int64_t)t * H, H, lane) : __builtin_nanf("");
+  if (lane == 0) {
+    lse2_out[row] = lse2;
+    zt2_out[row] = to_log2(zt);
+    row_loss[row] = (lse2 - to_log2(zt)) * kLn2;
+  }
+}
+
+// Vocabulary-chunked gradient of one chunk of columns [v0, v0 + n): u -> G
+// in place with the rows' lse2 from every chunk, and the target's element
+// (when it falls in the chunk) rewritten as (2^(zt2 - lse2) - 1) * scale.
+template <int UNROLL>
+__global__ void __launch_bounds__(64 * kWavesPerBlock)
+ce_rewrite_exp_kernel(uint16_t* __restrict__ u, int64_t ldu, const float* __restrict__ row_part,
+                      int64_t ldp, const float* __restrict__ lse2_in,
+                      const float* __restrict__ zt2_in, const int32_t* __restrict__ targets,
+                      int rows, int v0, int n, float scale) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float lse2 = lse2_in[row];
+  uint16_t* ur = u + (int64_t)row * ldu;
+  rescale_row<UNROLL>(ur, row_part + (int64_t)row * ldp, n, lse2 - log2_hw(scale), lane);
+  const int t = targets[row] - v0;
+  if (t >= 0 && t < n && lane == 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    const float pt = exp2_hw(zt2_in[row] - lse2);
     ur[t] = (uint16_t)bf16_bits((pt - 1.0f) * scale);
   }
 }
@@ -445,6 +515,33 @@ hipError_t launch_ce_rows_exp(uint16_t* u, int64_t ldu, const float* row_part, i
   const dim3 block(64 * kWavesPerBlock);
   hipLaunchKernelGGL((ce_rows_exp_kernel<4>), grid, block, 0, s, u, ldu, row_part, ldp, h, W, H,
                      targets, rows, V, scale, row_loss, loss_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_stats_exp(const float* row_part, int64_t ldp, const uint16_t* h,
+                               const uint16_t* W, int H, const int32_t* targets, int rows, int V,
+                               float* lse2, float* zt2, float* row_loss, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if ((H % 8) || (reinterpret_cast<uintptr_t>(h) & 15) || (reinterpret_cast<uintptr_t>(W) & 15) ||
+      ldp < 2 * ((V + kHalfTile - 1) / kHalfTile))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ce_stats_exp_kernel, dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock),
+                     dim3(64 * kWavesPerBlock), 0, s, row_part, ldp, h, W, H, targets, rows, V,
+                     lse2, zt2, row_loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_rewrite_exp(uint16_t* u, int64_t ldu, const float* row_part, int64_t ldp,
+                                 const float* lse2, const float* zt2, const int32_t* targets,
+                                 int rows, int v0, int n, float scale, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  // 16-byte pieces of u rows; the chunk starts on a half tile.
+  if ((n % 8) || (v0 % kHalfTile) || (ldu % 8) || (reinterpret_cast<uintptr_t>(u) & 15) ||
+      ldp < 2 * ((n + kHalfTile - 1) / kHalfTile))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((ce_rewrite_exp_kernel<4>), dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock),
+                     dim3(64 * kWavesPerBlock), 0, s, u, ldu, row_part, ldp, lse2, zt2, targets,
+                     rows, v0, n, scale);
   return hipGetLastError();
 }
 

@@ -342,13 +342,143 @@ extern "C" flce_status flce_cross_entropy(void* logits, int64_t ld, const int32_
              : FLCE_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Vocabulary-chunked variant (page 1, "Liger Kernel explained", section
+// "What does Liger Kernel actually fuse, and why does that cut memory?":
+// the logits are worked through in chunks over the vocabulary dimension).
+// All N tokens at once, the vocabulary in column chunks of Vc:
+//   pass 1  per chunk: exponentiated bf16 logits and their (max, sum) pairs
+//           (the values are not kept); then per row lse2 over all V columns,
+//           log2 of the target logit, the row loss; the mean loss
+//   pass 2  per chunk: the logits again, G over the chunk's columns with the
+//           global lse, grad_h (+)= G W_c into an fp32 [N, H] accumulator,
+//           grad_W[chunk rows] = G^T h
+//   finally grad_h = bf16(accumulator).
+// The logits are computed twice: 8 N V H flops instead of 6 N V H, for a
+// workspace of N Vc (not C V) bf16 logits.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct VocabLayout {
+  int64_t pairs, stats, acc, total;
+};
+inline VocabLayout vocab_layout(int64_t N, int64_t H, int64_t V, int64_t Vc) {
+  VocabLayout l;
+  l.pairs = round_up(N * Vc * 2, 256);                         // u [N][Vc] bf16
+  l.stats = round_up(l.pairs + N * n_half_tiles(V) * 8, 256);  // pairs [N][2 ceil(V/128)]
+  l.acc = round_up(l.stats + 3 * N * 4, 256);                  // lse2, zt2, row loss [N]
+  l.total = l.acc + N * H * 4;                                 // grad_h accumulator fp32
+  return l;
+}
+
+// Shapes the vocabulary-chunked path runs: bf16, K = H and every chunk's
+// K = Vc a multiple of 64 on the direct-to-LDS kernel, chunks starting on
+// 128-column half tiles.
+inline bool vocab_path_ok(int64_t H, int64_t V, int64_t vchunk, flce_dtype dt) {
+  return dt == FLCE_BF16 && H % 64 == 0 && H < (int64_t{1} << 22) && V % 64 == 0 &&
+         V < (int64_t{1} << 22) && (vchunk >= V || vchunk % flce::kHalfTile == 0) &&
+         flce::gemm_bf16_dma_enabled();
+}
+
+}  // namespace
+
+extern "C" size_t flce_vocab_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t vchunk,
+                                             flce_dtype dt) {
+  if (!dims_ok(N) || !dims_ok(H) || !dims_ok(V) || vchunk < 1 || !dtype_ok(dt)) return 0;
+  if (!vocab_path_ok(H, V, vchunk, dt)) return 0;
+  const int64_t Vc = vchunk < V ? vchunk : V;
+  return static_cast<size_t>(vocab_layout(N, H, V, Vc).total);
+}
+
+extern "C" flce_status flce_fwd_bwd_vocab(const void* h, const void* W, const int32_t* targets,
+                                          int64_t N, int64_t H, int64_t V, int64_t vchunk,
+                                          float* loss, void* grad_h, float* grad_W,
+                                          void* workspace, size_t workspace_bytes,
+                                          flce_dtype dt, hipStream_t stream) {
+  if (!h || !W || !targets || !loss || !grad_h || !grad_W || !workspace)
+    return FLCE_ERR_INVALID_ARG;
+  if (!dims_ok(N) || !dims_ok(H) || !dims_ok(V) || vchunk < 1 || !dtype_ok(dt))
+    return FLCE_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(W) || !aligned16(grad_h) || !aligned16(grad_W) ||
+      !aligned16(workspace) || (reinterpret_cast<uintptr_t>(targets) & 3u) ||
+      (reinterpret_cast<uintptr_t>(loss) & 3u))
+    return FLCE_ERR_UNSUPPORTED;
+  if (!vocab_path_ok(H, V, vchunk, dt)) return FLCE_ERR_UNSUPPORTED;
+  if (workspace_bytes < flce_vocab_workspace_bytes(N, H, V, vchunk, dt))
+    return FLCE_ERR_WORKSPACE;
+
+  const int64_t Vc = vchunk < V ? vchunk : V;
+  const VocabLayout lay = vocab_layout(N, H, V, Vc);
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* u = reinterpret_cast<uint16_t*>(ws);
+  float* pairs = reinterpret_cast<float*>(ws + lay.pairs);
+  float* lse2 = reinterpret_cast<float*>(ws + lay.stats);
+  float* zt2 = lse2 + N;
+  float* row_loss = zt2 + N;
+  float* gacc = reinterpret_cast<float*>(ws + lay.acc);
+  const int64_t ldp = 2 * n_half_tiles(V);
+  const int rows = static_cast<int>(N);
+  const float inv_n = static_cast<float>(1.0 / static_cast<double>(N));
+  const uint16_t* h16 = static_cast<const uint16_t*>(h);
+  const uint16_t* W16 = static_cast<const uint16_t*>(W);
+
+  // Exponentiated logits of columns [v0, v0 + n) for all tokens.
+  auto logits = [&](int64_t v0, int64_t n) {
+    flce::GemmArgs g{W16 + v0 * H, H, h, H, u, Vc, static_cast<int>(n), rows,
+                     static_cast<int>(H), 0};
+    g.group_m = 4;
+    g.stagger = 37;
+    g.row_part = pairs + 2 * (v0 / flce::kHalfTile);
+    g.ldp = ldp;
+    return flce::launch_gemm_bf16(true, true, flce::kExpBF16, true, g, stream);
+  };
+
+  // Pass 1: statistics.
+  for (int64_t v0 = 0; v0 < V; v0 += Vc)
+    if (logits(v0, (V - v0) < Vc ? (V - v0) : Vc) != hipSuccess) return FLCE_ERR_HIP;
+  if (flce::launch_ce_stats_exp(pairs, ldp, h16, W16, static_cast<int>(H), targets, rows,
+                                static_cast<int>(V), lse2, zt2, row_loss, stream) != hipSuccess ||
+      flce::launch_loss_sum(row_loss, 1, rows, inv_n, 1, loss, stream) != hipSuccess)
+    return FLCE_ERR_HIP;
+
+  // Pass 2: gradients, chunk by chunk.
+  for (int64_t v0 = 0; v0 < V; v0 += Vc) {
+    const int64_t n = (V - v0) < Vc ? (V - v0) : Vc;
+    if (logits(v0, n) != hipSuccess) return FLCE_ERR_HIP;
+    if (flce::launch_ce_rewrite_exp(u, Vc, pairs + 2 * (v0 / flce::kHalfTile), ldp, lse2, zt2,
+                                    targets, rows, static_cast<int>(v0), static_cast<int>(n),
+                                    inv_n, stream) != hipSuccess)
+      return FLCE_ERR_HIP;
+    // grad_h^T (+)= W_c^T . G^T: A(m = hidden, k = vocab) = W[v0 + k][m],
+    // B(n = token, k = vocab) = G[n][k]; fp32, accumulated after chunk 0.
+    flce::GemmArgs g4{W16 + v0 * H, H, u, Vc, gacc, H, static_cast<int>(H), rows,
+                      static_cast<int>(n), v0 > 0 ? 1 : 0};
+    g4.group_m = 4;
+    if (flce::launch_gemm_bf16(false, true, flce::kAccumF32, true, g4, stream) != hipSuccess)
+      return FLCE_ERR_HIP;
+    // grad_W[v0 + n][m] = sum over tokens k of G[k][n] h[k][m]:
+    // A(m = hidden, k = token) = h[k][m], B(n = vocab, k = token) = G[k][n].
+    flce::GemmArgs g5{h, H, u, Vc, grad_W + v0 * H, H, static_cast<int>(H), static_cast<int>(n),
+                      rows, 0};
+    g5.group_m = 4;
+    g5.stagger = 37;
+    if (flce::launch_gemm_bf16(false, false, flce::kAccumF32, true, g5, stream) != hipSuccess)
+      return FLCE_ERR_HIP;
+  }
+  return flce::launch_sum_parts_bf16(gacc, 1, N * H, static_cast<uint16_t*>(grad_h), N * H,
+                                     stream) == hipSuccess
+             ? FLCE_OK
+             : FLCE_ERR_HIP;
+}
+
 extern "C" const char* flce_status_string(flce_status s) {
   switch (s) {
     case FLCE_OK: return "FLCE_OK";
     case FLCE_ERR_INVALID_ARG: return "FLCE_ERR_INVALID_ARG: null pointer, bad size or dtype";
     case FLCE_ERR_WORKSPACE: return "FLCE_ERR_WORKSPACE: workspace smaller than required";
     case FLCE_ERR_UNSUPPORTED:
-      return "FLCE_ERR_UNSUPPORTED: H % 8 != 0 or a pointer is not 16-byte aligned";
+      return "FLCE_ERR_UNSUPPORTED: H % 8 != 0, a pointer not 16-byte aligned, or a shape "
+             "this entry point does not run";
     case FLCE_ERR_HIP: return "FLCE_ERR_HIP: the HIP runtime reported a launch error";
   }
   return "unknown flce_status";

@@ -97,6 +97,19 @@ hipError_t launch_ce_rows_exp(uint16_t* u, int64_t ldu, const float* row_part, i
                               const int32_t* targets, int rows, int V, float scale,
                               float* row_loss, int64_t loss_stride, hipStream_t s);
 
+// Vocabulary-chunked path, statistics: per row, lse2 over all V columns
+// from the pairs (row pitch ldp floats, 2 * ceil(V / 128) used), zt2 =
+// log2(e) * h_i . W_{t_i}, and row_loss = (lse2 - zt2) ln 2; [rows] each.
+hipError_t launch_ce_stats_exp(const float* row_part, int64_t ldp, const uint16_t* h,
+                               const uint16_t* W, int H, const int32_t* targets, int rows, int V,
+                               float* lse2, float* zt2, float* row_loss, hipStream_t s);
+// Vocabulary-chunked path, gradient of columns [v0, v0 + n) (v0 % 128 == 0,
+// n % 8 == 0): u (row pitch ldu) -> (u 2^(mx_q - lse2) - [j == t]) * scale
+// in place; row_part points at the chunk's first pair of row 0.
+hipError_t launch_ce_rewrite_exp(uint16_t* u, int64_t ldu, const float* row_part, int64_t ldp,
+                                 const float* lse2, const float* zt2, const int32_t* targets,
+                                 int rows, int v0, int n, float scale, hipStream_t s);
+
 // out[i] = bf16(sum over s < S of parts[s * stride + i]) for i < n, summed
 // in the order s = 0, 1, ... (deterministic); parts and out 16-byte aligned.
 hipError_t launch_sum_parts_bf16(const float* parts, int S, int64_t stride, uint16_t* out,

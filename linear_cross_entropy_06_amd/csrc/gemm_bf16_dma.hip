@@ -657,6 +657,8 @@ hipError_t launch_gemm_bf16_dma(bool a_kc, bool b_kc, int epi, const GemmArgs& g
     return launch_dma<false, true, kStoreOut, uint16_t>(g, s);
   if (!a_kc && b_kc && epi == kStoreF32)  // K-split parts of grad_h
     return launch_dma<false, true, kStoreF32, float>(g, s);
+  if (!a_kc && b_kc && epi == kAccumF32)  // fp32 grad_h over vocabulary chunks
+    return launch_dma<false, true, kAccumF32, float>(g, s);
   if (!a_kc && !b_kc && epi == kAccumF32)
     return launch_dma<false, false, kAccumF32, float>(g, s);
   return hipErrorInvalidValue;

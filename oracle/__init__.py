@@ -13,6 +13,7 @@ from .flce_oracle import (
     flce_brute,
     flce_chunked,
     flce_sampled,
+    flce_vocab_chunked,
     logits,
     logsumexp_rows,
     row_losses,
@@ -24,6 +25,7 @@ __all__ = [
     "flce_brute",
     "flce_chunked",
     "flce_sampled",
+    "flce_vocab_chunked",
     "logits",
     "logsumexp_rows",
     "row_losses",

@@ -35,10 +35,13 @@ every target is a valid class (no ignore index); there is no bias, label
 smoothing, z-loss, soft-capping or temperature; h is [N, H] and W is [V, H],
 row-major.
 
-Three implementations, all fp64:
+Four implementations, all fp64:
 * ``flce``          the definition above, unchunked (small inputs);
 * ``flce_chunked``  the same steps over token chunks, grad_W accumulated in
                     fp64 and the 1/N taken with the global N (any size);
+* ``flce_vocab_chunked``  the same result over chunks of vocabulary rows:
+                    a pass of running (max, sum) statistics, then the
+                    gradients chunk by chunk with the global log-sum-exp;
 * ``flce_brute``    pure-Python loops (tiny inputs; pins numpy's matmul and
                     broadcasting);
 and ``flce_sampled`` for full-size checks: the loss plus chosen rows of
@@ -123,6 +126,56 @@ def flce_chunked(h: np.ndarray, W: np.ndarray, t: np.ndarray, chunk: int):
         grad_h[r0:r1] = G @ W
         grad_W += G.T @ h[r0:r1]
     return float(loss_sum / N), grad_h, grad_W
+
+
+def flce_vocab_chunked(h: np.ndarray, W: np.ndarray, t: np.ndarray, vchunk: int):
+    """The same result computed over chunks of ``vchunk`` vocabulary rows of W
+    (page 1, "Liger Kernel explained", section "What does Liger Kernel
+    actually fuse, and why does that cut memory?": the logits are worked
+    through in chunks over the vocabulary dimension).
+
+    Only an [N, vchunk] block of logits exists at a time.  Pass 1 keeps, per
+    row, the running maximum m and the sum s of exp(Z - m) over the chunks
+    seen so far (when a chunk raises the maximum, the old sum is rescaled by
+    exp(m_old - m_new)), which gives lse = m + ln s and the row loss (the
+    target's logit is read in the chunk that holds it).  Pass 2 forms every
+    chunk's logits again, its dloss/dZ with the global lse, adds G W_c to
+    grad_h and writes G^T h into the chunk's rows of grad_W.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    t = np.asarray(t, dtype=np.int64)
+    _check(h, W, t)
+    if vchunk < 1:
+        raise ValueError("vchunk must be >= 1")
+    N, V = h.shape[0], W.shape[0]
+    rows = np.arange(N)
+    m = np.full(N, -np.inf)
+    s = np.zeros(N)
+    zt = np.empty(N)
+    for v0 in range(0, V, vchunk):
+        v1 = min(V, v0 + vchunk)
+        Z = logits(h, W[v0:v1])
+        mc = Z.max(axis=1)
+        m_new = np.maximum(m, mc)
+        s = s * np.exp(m - m_new) + np.exp(Z - m_new[:, None]).sum(axis=1)
+        m = m_new
+        inside = (t >= v0) & (t < v1)
+        zt[inside] = Z[rows[inside], t[inside] - v0]
+    lse = m + np.log(s)
+    loss = float((lse - zt).sum() / N)
+    grad_h = np.zeros_like(h)
+    grad_W = np.empty_like(W)
+    for v0 in range(0, V, vchunk):
+        v1 = min(V, v0 + vchunk)
+        Z = logits(h, W[v0:v1])
+        G = np.exp(Z - lse[:, None])
+        inside = (t >= v0) & (t < v1)
+        G[rows[inside], t[inside] - v0] -= 1.0
+        G /= N
+        grad_h += G @ W[v0:v1]
+        grad_W[v0:v1] = G.T @ h
+    return loss, grad_h, grad_W
 
 
 def flce_brute(h, W, t):

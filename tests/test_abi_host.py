@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     assert names == sorted(["flce_workspace_bytes", "flce_fwd_bwd", "flce_launch_count",
                             "flce_fwd_bwd_timed", "flce_logits", "flce_ce_rows",
                             "flce_fwd_bwd_accumulate", "flce_scale_grads",
-                            "flce_cross_entropy", "flce_status_string"])
+                            "flce_cross_entropy", "flce_fwd_bwd_vocab",
+                            "flce_vocab_workspace_bytes", "flce_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -170,6 +171,56 @@ def test_cross_entropy_validates(lib):
     assert f(P + 1, 8, P, 4, 5, P, P, BF16, None) == UNSUPPORTED
     assert f(P + 2, 8, P, 4, 5, P, P, F32, None) == UNSUPPORTED
     assert f(P, 8, P + 2, 4, 5, P, P, BF16, None) == UNSUPPORTED
+
+
+def test_vocab_workspace_bytes(lib):
+    f = lib.flce_vocab_workspace_bytes
+    rup = lambda x: (x + 255) // 256 * 256
+
+    def formula(N, H, V, vc):
+        c = min(vc, V)
+        a = rup(N * c * 2)
+        b = rup(a + N * ((V + 127) // 128) * 8)
+        d = rup(b + 3 * N * 4)
+        return d + N * H * 4
+
+    for args in [(8192, 4096, 128256, 16384), (1024, 3584, 256000, 32768), (300, 128, 1024, 256),
+                 (5, 64, 640, 10 ** 6)]:
+        assert f(*args, BF16) == formula(*args), args
+    # below the token-chunked workspace of one 4096-token chunk
+    assert f(8192, 4096, 128256, 16384, BF16) < lib.flce_workspace_bytes(8192, 4096, 128256,
+                                                                         4096, BF16)
+    # shapes the entry point does not run, and bad sizes
+    for bad in [(300, 136, 1024, 256, BF16),   # H % 64
+                (300, 128, 1000, 256, BF16),   # V % 64
+                (300, 128, 1024, 200, BF16),   # vchunk % 128 (and < V)
+                (300, 128, 1024, 256, F32),    # dtype
+                (0, 128, 1024, 256, BF16), (300, 128, 1024, 0, BF16)]:
+        assert f(*bad) == 0, bad
+
+
+def _vcall(lib, **kw):
+    a = dict(h=P, W=P, t=P, N=4, H=64, V=128, vc=128, loss=P, gh=P, gW=P, ws=P,
+             wsb=1 << 30, dt=BF16, stream=None)
+    a.update(kw)
+    return lib.flce_fwd_bwd_vocab(a["h"], a["W"], a["t"], a["N"], a["H"], a["V"], a["vc"],
+                                  a["loss"], a["gh"], a["gW"], a["ws"], a["wsb"], a["dt"],
+                                  a["stream"])
+
+
+def test_vocab_entry_validates(lib):
+    for field in ["h", "W", "t", "loss", "gh", "gW", "ws"]:
+        assert _vcall(lib, **{field: None}) == INVALID, field
+    for field, value in [("N", 0), ("H", -1), ("V", 0), ("vc", 0), ("dt", 5)]:
+        assert _vcall(lib, **{field: value}) == INVALID, field
+    for field in ["h", "W", "gh", "gW", "ws"]:
+        assert _vcall(lib, **{field: P + 8}) == UNSUPPORTED, field
+    assert _vcall(lib, H=72) == UNSUPPORTED          # H % 64
+    assert _vcall(lib, V=100) == UNSUPPORTED         # V % 64
+    assert _vcall(lib, V=512, vc=192) == UNSUPPORTED  # vchunk % 128
+    assert _vcall(lib, dt=F32) == UNSUPPORTED
+    need = lib.flce_vocab_workspace_bytes(4, 64, 128, 128, BF16)
+    assert _vcall(lib, wsb=need - 1) == WORKSPACE
 
 
 def test_status_strings(lib):

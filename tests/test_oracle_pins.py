@@ -24,7 +24,7 @@ import pytest
 import torch
 
 import oracle
-from oracle import flce, flce_brute, flce_chunked, flce_sampled
+from oracle import flce, flce_brute, flce_chunked, flce_sampled, flce_vocab_chunked
 
 RTOL = 1e-11
 
@@ -209,12 +209,20 @@ def _chunked(c):
     return lambda h, W, t: flce_chunked(h, W, t, c)
 
 
+def _vocab_chunked(c):
+    return lambda h, W, t: flce_vocab_chunked(h, W, t, c)
+
+
 IMPLS = {
     "plain": flce,
     "chunk1": _chunked(1),
     "chunk2": _chunked(2),
     "chunk3": _chunked(3),
     "chunk_big": _chunked(1000),
+    "vchunk1": _vocab_chunked(1),
+    "vchunk2": _vocab_chunked(2),
+    "vchunk3": _vocab_chunked(3),
+    "vchunk_big": _vocab_chunked(1000),
     "sampled_all_rows": None,  # filled below
 }
 
@@ -247,6 +255,22 @@ def test_chunked_equals_unchunked_tiny():
         assert abs(l0 - l1) <= 1e-14 * max(1, abs(l0))
         _close(gh1, gh0, rtol=1e-14)
         _close(gw1, gw0, rtol=1e-14)
+
+
+def test_vocab_chunked_equals_unchunked():
+    """Vocabulary chunks (running max/sum merge, then the gradients chunk by
+    chunk) reach the unchunked result, including chunks whose maximum is
+    below an earlier chunk's and logits large enough that exp overflows
+    without the shift."""
+    for (N, H, V, seed, w_std) in [(7, 5, 9, 22, 0.5), (5, 16, 40, 23, 20.0)]:
+        h, W, t = _rand(N, H, V, seed=seed, w_std=w_std)
+        l0, gh0, gw0 = flce(h, W, t)
+        for c in (1, 2, 4, V - 1, V, 3 * V):
+            l1, gh1, gw1 = flce_vocab_chunked(h, W, t, c)
+            assert np.isfinite(l1)
+            assert abs(l0 - l1) <= 1e-12 * max(1, abs(l0))
+            _close(gh1, gh0, rtol=1e-12)
+            _close(gw1, gw0, rtol=1e-12)
 
 
 def test_large_logits_stay_finite():
@@ -384,6 +408,45 @@ def _mut_last_chunk_only(h, W, t):
     return loss, gh, gw
 
 
+def _mut_vocab_merge_without_rescale(h, W, t):
+    # vocabulary chunks whose sums are added without rescaling to the new max
+    N, V = h.shape[0], W.shape[0]
+    c = 2
+    m = np.full(N, -np.inf)
+    s = np.zeros(N)
+    for v0 in range(0, V, c):
+        Z = h @ W[v0:v0 + c].T
+        mc = Z.max(axis=1)
+        s = s + np.exp(Z - mc[:, None]).sum(axis=1)
+        m = np.maximum(m, mc)
+    lse = m + np.log(s)
+    Z = h @ W.T
+    loss = float((lse - Z[np.arange(N), t]).sum() / N)
+    G = np.exp(Z - lse[:, None])
+    G[np.arange(N), t] -= 1.0
+    G /= N
+    return loss, G @ W, G.T @ h
+
+
+def _mut_vocab_local_lse(h, W, t):
+    # each vocabulary chunk's gradient normalised by its own log-sum-exp
+    N, V = h.shape[0], W.shape[0]
+    c = 3
+    l0, _, _ = flce(h, W, t)
+    gh = np.zeros_like(h)
+    gw = np.empty_like(W)
+    for v0 in range(0, V, c):
+        v1 = min(V, v0 + c)
+        Z = h @ W[v0:v1].T
+        G = np.exp(Z - oracle.logsumexp_rows(Z)[:, None])
+        inside = (t >= v0) & (t < v1)
+        G[np.arange(N)[inside], t[inside] - v0] -= 1.0
+        G /= N
+        gh += G @ W[v0:v1]
+        gw[v0:v1] = G.T @ h
+    return l0, gh, gw
+
+
 def _mut_transposed_h(h, W, t):
     # grad_h computed with W's columns permuted (a transposed-index slip)
     l, gh, gw = flce(h, W, t)
@@ -400,6 +463,8 @@ MUTANTS = [
     _mut_softmax_wrong_axis,
     _mut_grad_w_uses_w,
     _mut_last_chunk_only,
+    _mut_vocab_merge_without_rescale,
+    _mut_vocab_local_lse,
     _mut_transposed_h,
 ]
 
