@@ -52,10 +52,11 @@ def parse_args():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=4096)
-    p.add_argument("--op", choices=("flce", "ce", "vocab"), default="flce",
+    p.add_argument("--op", choices=("flce", "ce", "vocab", "rmsnorm"), default="flce",
                    help="flce: the fused head (default); ce: cross entropy on given bf16 "
                         "logits [1024, 128256] (flce_cross_entropy); vocab: the fused head "
-                        "through flce_fwd_bwd_vocab (vocabulary chunks)")
+                        "through flce_fwd_bwd_vocab (vocabulary chunks); rmsnorm: the head "
+                        "behind an RMSNorm (flce_fwd_bwd_rmsnorm)")
     p.add_argument("--vchunk", type=int, default=16384,
                    help="vocabulary chunk of --op vocab")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -280,13 +281,78 @@ def bench_vocab(args) -> int:
     return 0
 
 
+def bench_rmsnorm(args) -> int:
+    """The fused head behind an RMSNorm (flce_fwd_bwd_rmsnorm) on a workload:
+    the workload's hidden states are the norm's input x, gamma is a seeded
+    weight near 1, eps 1e-6.  Same token chunk as the default bench."""
+    import torch
+
+    import linear_cross_entropy_06_amd as flce
+    from synth import config_by_name, make_inputs, make_norm_weight
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    flce.load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg = config_by_name(args.workload)
+    inp = make_inputs(cfg, seed=args.seed)
+    x, W, t = inp.h.to(dev), inp.W.to(dev), inp.t.to(dev)
+    g = make_norm_weight(cfg.H, seed=args.seed).to(dev)
+    N, H, V = cfg.N, cfg.H, cfg.V
+    C = args.chunk or cfg.default_chunk
+    need = flce.rmsnorm_workspace_bytes(N, H, V, C, x.dtype)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    kw = dict(loss=torch.empty((), dtype=torch.float32, device=dev), grad_x=torch.empty_like(x),
+              grad_gamma=torch.empty(H, dtype=torch.float32, device=dev),
+              grad_W=torch.empty((V, H), dtype=torch.float32, device=dev), workspace=ws)
+    for _ in range(max(1, args.warmup)):
+        flce.fwd_bwd_rmsnorm(x, g, W, t, C, 1e-6, **kw)
+    torch.cuda.synchronize()
+    loss0 = float(kw["loss"])
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        flce.fwd_bwd_rmsnorm(x, g, W, t, C, 1e-6, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    flops = 6.0 * N * V * H
+    out = {
+        "metric": "FLCE fwd+bwd tokens/s (behind an RMSNorm, flce_fwd_bwd_rmsnorm)",
+        "value": N / (ms * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; the workload's hidden states as the norm input)",
+        "config": {"workload": cfg.name, "N": N, "H": H, "V": V, "chunk": C, "eps": 1e-6,
+                   "seed": args.seed},
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "workspace_bytes": need,
+        "loss": loss0,
+        "roofline": {
+            "kernel": "fwd_bwd_rmsnorm (all launches of one call)", "bound": "mfma",
+            "achieved": flops / (ev_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": flops / (ev_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "traffic": None, "work_per_launch": f"6*{N}*{V}*{H} = {flops:.4e} flop",
+        },
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
-    if args.op in ("ce", "vocab"):
+    if args.op in ("ce", "vocab", "rmsnorm"):
         if args.gpus != 1:
             print("bench.py: this build runs on one GPU only", file=sys.stderr)
             return 2
-        return bench_ce(args) if args.op == "ce" else bench_vocab(args)
+        return {"ce": bench_ce, "vocab": bench_vocab, "rmsnorm": bench_rmsnorm}[args.op](args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "

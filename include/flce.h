@@ -210,6 +210,48 @@ flce_status flce_cross_entropy(void* logits, int64_t ld, const int32_t* targets,
                                flce_dtype dt, hipStream_t stream);
 
 /*
+ * The fused head behind an RMSNorm of its input (page 3, "Complete Guide to
+ * Liger Kernel", section "LigerRMSNorm"; the epsilon convention of page 2,
+ * section "The support surface is narrower than the pitch suggests", is eps
+ * added to the mean square):
+ *   r_i    = 1 / sqrt(mean_k x[i, k]^2 + eps)
+ *   h      = x * r * gamma           (per row; rounded once to dt)
+ * followed by flce_fwd_bwd on h, and the chain rule back through the norm:
+ *   grad_x[i, k]  = r_i gamma_k g[i, k] - x[i, k] r_i^3 / H sum_k gamma_k g[i, k] x[i, k]
+ *   grad_gamma[k] = sum_i g[i, k] x[i, k] r_i
+ * with g = dloss/dh.  Each token chunk is normalised into the workspace just
+ * before its logits and the norm's backward runs right after the chunk's
+ * gradients, so h and dloss/dh exist for one chunk at a time.
+ *
+ *  x          [N, H]  dt     pre-norm hidden states (read only)
+ *  gamma      [H]     dt     norm weight (read only, 16-byte aligned)
+ *  eps               fp32   >= 0 and finite (FLCE_ERR_INVALID_ARG otherwise);
+ *                            with eps = 0 an all-zero row gives a non-finite
+ *                            result
+ *  W, targets, N, H, V, chunk, loss, grad_W, stream: as flce_fwd_bwd
+ *  grad_x     [N, H]  dt     overwritten with dloss/dx
+ *  grad_gamma [H]     fp32   overwritten with dloss/dgamma (4-byte aligned)
+ *  workspace                 >= flce_rmsnorm_workspace_bytes(N, H, V, chunk, dt)
+ * The gradients are those of the mean loss with an upstream gradient of 1.
+ */
+flce_status flce_fwd_bwd_rmsnorm(const void* x, const void* gamma, float eps, const void* W,
+                                 const int32_t* targets, int64_t N, int64_t H, int64_t V,
+                                 int64_t chunk, float* loss, void* grad_x, float* grad_gamma,
+                                 float* grad_W, void* workspace, size_t workspace_bytes,
+                                 flce_dtype dt, hipStream_t stream);
+
+/*
+ * Bytes of workspace flce_fwd_bwd_rmsnorm needs, with C = min(chunk, N) and
+ * es the element size of dt: flce_workspace_bytes(N, H, V, chunk, dt), then
+ * (each region starting on a 256-byte boundary) C * H * es for the chunk's
+ * h, C * H * es for its dloss/dh, C * 4 for the per-row 1/rms, and
+ * ceil(C / 64) * H * 4 for the grad_gamma partial sums.  0 when a size is
+ * < 1.  Pure host function.
+ */
+size_t flce_rmsnorm_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk,
+                                    flce_dtype dt);
+
+/*
  * Vocabulary-chunked variant of flce_fwd_bwd (page 1, "Liger Kernel
  * explained", section "What does Liger Kernel actually fuse, and why does
  * that cut memory?": the logits are worked through in chunks over the

@@ -19,11 +19,13 @@ from ._lib import (
     cross_entropy,
     cross_entropy_,
     fwd_bwd,
+    fwd_bwd_rmsnorm,
     fwd_bwd_vocab,
     launch_count,
     linear_cross_entropy,
     load,
     logits,
+    rmsnorm_workspace_bytes,
     scale_grads,
     vocab_workspace_bytes,
     workspace_bytes,
@@ -44,11 +46,13 @@ __all__ = [
     "cross_entropy",
     "cross_entropy_",
     "fwd_bwd",
+    "fwd_bwd_rmsnorm",
     "fwd_bwd_vocab",
     "launch_count",
     "linear_cross_entropy",
     "load",
     "logits",
+    "rmsnorm_workspace_bytes",
     "scale_grads",
     "vocab_workspace_bytes",
     "workspace_bytes",

@@ -42,6 +42,8 @@ EXPORTS = (
     "flce_cross_entropy",
     "flce_fwd_bwd_vocab",
     "flce_vocab_workspace_bytes",
+    "flce_fwd_bwd_rmsnorm",
+    "flce_rmsnorm_workspace_bytes",
     "flce_status_string",
 )
 
@@ -93,6 +95,11 @@ def load() -> ctypes.CDLL:
     lib.flce_fwd_bwd_vocab.restype = ctypes.c_int
     lib.flce_vocab_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.flce_vocab_workspace_bytes.restype = sz
+    lib.flce_fwd_bwd_rmsnorm.argtypes = [vp, vp, ctypes.c_float, vp, vp, i64, i64, i64, i64,
+                                         vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
+    lib.flce_fwd_bwd_rmsnorm.restype = ctypes.c_int
+    lib.flce_rmsnorm_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.flce_rmsnorm_workspace_bytes.restype = sz
     lib.flce_status_string.argtypes = [ctypes.c_int]
     lib.flce_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -265,6 +272,58 @@ def fwd_bwd_vocab(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, vchun
                                 _stream_ptr(dev))
     _check(st)
     return loss, grad_h, grad_W
+
+
+def rmsnorm_workspace_bytes(N: int, H: int, V: int, chunk: int, dtype: torch.dtype) -> int:
+    """Workspace of ``flce_fwd_bwd_rmsnorm``."""
+    dt = FLCE_BF16 if dtype == torch.bfloat16 else FLCE_F32
+    return int(load().flce_rmsnorm_workspace_bytes(N, H, V, chunk, dt))
+
+
+def fwd_bwd_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, W: torch.Tensor,
+                    targets: torch.Tensor, chunk: Optional[int] = None, eps: float = 1e-6, *,
+                    loss: Optional[torch.Tensor] = None,
+                    grad_x: Optional[torch.Tensor] = None,
+                    grad_gamma: Optional[torch.Tensor] = None,
+                    grad_W: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None,
+                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Mean cross-entropy loss of rmsnorm(x; gamma, eps) W^T against targets
+    via ``flce_fwd_bwd_rmsnorm``.  Returns (loss [] fp32, grad_x like x,
+    grad_gamma [H] fp32, grad_W [V, H] fp32)."""
+    lib = load()
+    _need_cuda(x, gamma, W, targets)
+    if targets.dtype != torch.int32:
+        raise TypeError("targets must be int32")
+    if W.dtype != x.dtype or gamma.dtype != x.dtype:
+        raise TypeError("x, gamma and W must share a dtype")
+    N, H = x.shape
+    V = W.shape[0]
+    if gamma.shape != (H,):
+        raise ValueError("gamma must have shape [H]")
+    chunk = N if chunk is None else int(chunk)
+    dt = _dt(x)
+    dev = x.device
+    if loss is None:
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+    if grad_x is None:
+        grad_x = torch.empty_like(x)
+    if grad_gamma is None:
+        grad_gamma = torch.empty(H, dtype=torch.float32, device=dev)
+    if grad_W is None:
+        grad_W = torch.empty((V, H), dtype=torch.float32, device=dev)
+    need = int(lib.flce_rmsnorm_workspace_bytes(N, H, V, chunk, dt))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need_cuda(loss, grad_x, grad_gamma, grad_W, workspace)
+    st = lib.flce_fwd_bwd_rmsnorm(x.data_ptr(), gamma.data_ptr(), float(eps), W.data_ptr(),
+                                  targets.data_ptr(), N, H, V, chunk, loss.data_ptr(),
+                                  grad_x.data_ptr(), grad_gamma.data_ptr(), grad_W.data_ptr(),
+                                  workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), dt,
+                                  _stream_ptr(dev))
+    _check(st)
+    return loss, grad_x, grad_gamma, grad_W
 
 
 def logits(h: torch.Tensor, W: torch.Tensor, z: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -120,11 +120,27 @@ struct Marks {
   }
 };
 
+// An RMSNorm in front of the head (flce_fwd_bwd_rmsnorm): per token chunk,
+// h_c = rmsnorm(x_c) is formed into h_buf before step 1, step 4 writes
+// grad_h_c into g_buf, and after step 5 the norm's backward turns g_buf into
+// the chunk's grad_x rows and adds to grad_gamma.
+struct NormSide {
+  const void* x;
+  const void* gamma;
+  float eps;
+  void* grad_x;
+  float* grad_gamma;
+  char* h_buf;   // [C][H] dt
+  char* g_buf;   // [C][H] dt
+  float* rinv;   // [C]
+  float* part;   // [rmsnorm_groups(C)][H]
+};
+
 flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, int64_t N,
                          int64_t H, int64_t V, int64_t chunk, float* loss, void* grad_h,
                          float* grad_W, void* workspace, size_t workspace_bytes,
                          flce_dtype dt, hipStream_t stream, hipEvent_t* events,
-                         int64_t n_events, bool accumulate) {
+                         int64_t n_events, bool accumulate, const NormSide* ns = nullptr) {
   if (!h || !W || !targets || !loss || !grad_h || !grad_W || !workspace)
     return FLCE_ERR_INVALID_ARG;
   if (!dims_ok(N) || !dims_ok(H) || !dims_ok(V) || chunk < 1 || !dtype_ok(dt))
@@ -163,8 +179,16 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
     const int rows = static_cast<int>((N - r0) < C ? (N - r0) : C);
     const char* hc = static_cast<const char*>(h) + r0 * H * es;
     char* ghc = static_cast<char*>(grad_h) + r0 * H * es;
-    float* staged = reinterpret_cast<float*>(ghc);
     hipError_t e;
+    if (ns) {
+      // 0. h_c = rmsnorm(x_c) into the workspace; grad_h_c goes there too.
+      if (flce::launch_rmsnorm_fwd(hc, ns->gamma, ns->eps, rows, static_cast<int>(H), ns->h_buf,
+                                   ns->rinv, bf16, stream) != hipSuccess)
+        return FLCE_ERR_HIP;
+      hc = ns->h_buf;
+      ghc = ns->g_buf;
+    }
+    float* staged = reinterpret_cast<float*>(ghc);
 
     // 1. Z^T = W . h_c^T, stored as Z[i][j] (row pitch V), or as its
     //    exponentiated bf16 form with (max, sum) pairs.
@@ -236,6 +260,16 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
     e = gemm(dt, false, false, flce::kAccumF32, vec, g5, stream);
     mk.after();
     if (e != hipSuccess) return FLCE_ERR_HIP;
+
+    if (ns) {
+      // 6. the norm's backward: grad_x rows of the chunk, grad_gamma (+)=.
+      const char* xc = static_cast<const char*>(ns->x) + r0 * H * es;
+      char* gxc = static_cast<char*>(ns->grad_x) + r0 * H * es;
+      if (flce::launch_rmsnorm_bwd(xc, ns->gamma, ns->g_buf, ns->rinv, rows, static_cast<int>(H),
+                                   gxc, ns->part, ns->grad_gamma, r0 == 0 ? 1 : 0, bf16,
+                                   stream) != hipSuccess)
+        return FLCE_ERR_HIP;
+    }
   }
   return FLCE_OK;
 }
@@ -340,6 +374,72 @@ extern "C" flce_status flce_cross_entropy(void* logits, int64_t ld, const int32_
   return flce::launch_loss_sum(row_loss, 1, r, inv, 1, loss, stream) == hipSuccess
              ? FLCE_OK
              : FLCE_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// The head behind an RMSNorm (page 3, "Complete Guide to Liger Kernel",
+// section "LigerRMSNorm"): the caller passes the pre-norm hidden states x and
+// the norm weight gamma; each token chunk is normalised into the workspace
+// just before its logits, and the norm's backward runs right after the
+// chunk's gradients, so neither h nor grad_h exists for more than one chunk.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct NormLayout {
+  int64_t h_buf, g_buf, rinv, part, total;
+};
+inline NormLayout norm_layout(size_t base, int64_t C, int64_t H, int64_t es) {
+  NormLayout l;
+  l.h_buf = round_up(static_cast<int64_t>(base), 256);
+  l.g_buf = round_up(l.h_buf + C * H * es, 256);
+  l.rinv = round_up(l.g_buf + C * H * es, 256);
+  l.part = round_up(l.rinv + C * 4, 256);
+  l.total = l.part + static_cast<int64_t>(flce::rmsnorm_groups(static_cast<int>(C))) * H * 4;
+  return l;
+}
+
+}  // namespace
+
+extern "C" size_t flce_rmsnorm_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk,
+                                               flce_dtype dt) {
+  const size_t base = flce_workspace_bytes(N, H, V, chunk, dt);
+  if (base == 0) return 0;
+  const int64_t C = chunk < N ? chunk : N;
+  return static_cast<size_t>(norm_layout(base, C, H, esize(dt)).total);
+}
+
+extern "C" flce_status flce_fwd_bwd_rmsnorm(const void* x, const void* gamma, float eps,
+                                            const void* W, const int32_t* targets, int64_t N,
+                                            int64_t H, int64_t V, int64_t chunk, float* loss,
+                                            void* grad_x, float* grad_gamma, float* grad_W,
+                                            void* workspace, size_t workspace_bytes,
+                                            flce_dtype dt, hipStream_t stream) {
+  if (!x || !gamma || !grad_gamma || !W || !targets || !loss || !grad_x || !grad_W ||
+      !workspace)
+    return FLCE_ERR_INVALID_ARG;
+  if (!dims_ok(N) || !dims_ok(H) || !dims_ok(V) || chunk < 1 || !dtype_ok(dt))
+    return FLCE_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return FLCE_ERR_INVALID_ARG;  // NaN, negative or inf
+  if (H % 8 != 0) return FLCE_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(grad_x) || !aligned16(grad_W) ||
+      !aligned16(workspace) || (reinterpret_cast<uintptr_t>(grad_gamma) & 3u))
+    return FLCE_ERR_UNSUPPORTED;
+  const size_t need = flce_rmsnorm_workspace_bytes(N, H, V, chunk, dt);
+  if (workspace_bytes < need) return FLCE_ERR_WORKSPACE;
+  const int64_t C = chunk < N ? chunk : N;
+  const NormLayout lay = norm_layout(flce_workspace_bytes(N, H, V, chunk, dt), C, H, esize(dt));
+  char* ws = static_cast<char*>(workspace);
+  const NormSide ns{x,
+                    gamma,
+                    eps,
+                    grad_x,
+                    grad_gamma,
+                    ws + lay.h_buf,
+                    ws + lay.g_buf,
+                    reinterpret_cast<float*>(ws + lay.rinv),
+                    reinterpret_cast<float*>(ws + lay.part)};
+  return fwd_bwd_impl(x, W, targets, N, H, V, chunk, loss, grad_x, grad_W, workspace,
+                      workspace_bytes, dt, stream, nullptr, 0, false, &ns);
 }
 
 // ---------------------------------------------------------------------------

@@ -110,6 +110,18 @@ hipError_t launch_ce_rewrite_exp(uint16_t* u, int64_t ldu, const float* row_part
                                  const float* lse2, const float* zt2, const int32_t* targets,
                                  int rows, int v0, int n, float scale, hipStream_t s);
 
+// RMSNorm in front of the head (rmsnorm.hip), one wave per row, H % 8 == 0,
+// 16-byte aligned rows: h = x * r * gamma with r = 1/sqrt(mean x^2 + eps)
+// (r stored per row in rinv), and its backward from g = dloss/dh: grad_x
+// rows, and grad_gamma (fp32 [H]) = (first ? 0 : grad_gamma) + sum_i
+// g_i * x_i * r_i through `part` (rmsnorm_groups(rows) * H floats).
+int rmsnorm_groups(int rows);
+hipError_t launch_rmsnorm_fwd(const void* x, const void* gamma, float eps, int rows, int H,
+                              void* h, float* rinv, bool bf16, hipStream_t s);
+hipError_t launch_rmsnorm_bwd(const void* x, const void* gamma, const void* g, const float* rinv,
+                              int rows, int H, void* grad_x, float* part, float* grad_gamma,
+                              int first, bool bf16, hipStream_t s);
+
 // out[i] = bf16(sum over s < S of parts[s * stride + i]) for i < n, summed
 // in the order s = 0, 1, ... (deterministic); parts and out 16-byte aligned.
 hipError_t launch_sum_parts_bf16(const float* parts, int S, int64_t stride, uint16_t* out,

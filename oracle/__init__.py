@@ -12,10 +12,12 @@ from .flce_oracle import (
     flce,
     flce_brute,
     flce_chunked,
+    flce_rmsnorm,
     flce_sampled,
     flce_vocab_chunked,
     logits,
     logsumexp_rows,
+    rmsnorm,
     row_losses,
 )
 
@@ -24,9 +26,11 @@ __all__ = [
     "flce",
     "flce_brute",
     "flce_chunked",
+    "flce_rmsnorm",
     "flce_sampled",
     "flce_vocab_chunked",
     "logits",
     "logsumexp_rows",
+    "rmsnorm",
     "row_losses",
 ]

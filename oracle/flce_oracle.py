@@ -44,6 +44,8 @@ Four implementations, all fp64:
                     gradients chunk by chunk with the global log-sum-exp;
 * ``flce_brute``    pure-Python loops (tiny inputs; pins numpy's matmul and
                     broadcasting);
+``flce_rmsnorm`` puts an RMSNorm in front of the head (h = rmsnorm(x)) and
+returns the gradients of its input x and weight gamma by the chain rule;
 and ``flce_sampled`` for full-size checks: the loss plus chosen rows of
 grad_h and grad_W, without holding an [N, V] or [V, H] array.
 """
@@ -176,6 +178,37 @@ def flce_vocab_chunked(h: np.ndarray, W: np.ndarray, t: np.ndarray, vchunk: int)
         grad_h += G @ W[v0:v1]
         grad_W[v0:v1] = G.T @ h
     return loss, grad_h, grad_W
+
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float):
+    """RMSNorm of each row (page 3, "Complete Guide to Liger Kernel", section
+    "LigerRMSNorm"; the epsilon convention page 2 warns about, section "The
+    support surface is narrower than the pitch suggests", is eps added to the
+    mean square): h = x / sqrt(mean_k x_k^2 + eps) * gamma.  Returns (h, r)
+    with r = 1 / sqrt(mean_k x_k^2 + eps) per row."""
+    x = np.asarray(x, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    r = 1.0 / np.sqrt((x * x).mean(axis=1) + eps)
+    return x * r[:, None] * gamma[None, :], r
+
+
+def flce_rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float, W: np.ndarray, t: np.ndarray):
+    """The loss head behind an RMSNorm of its input: h = rmsnorm(x), then the
+    definition above.  Returns (loss, grad_x, grad_gamma, grad_W) by the chain
+    rule through h = x r gamma, r = (mean x^2 + eps)^(-1/2):
+
+        grad_x     = r (gamma * grad_h) - x r^3 / H * sum_k gamma_k grad_h_k x_k
+        grad_gamma = sum_i grad_h_i * x_i r_i
+    """
+    x = np.asarray(x, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    H = x.shape[1]
+    h, r = rmsnorm(x, gamma, eps)
+    loss, gh, gw = flce(h, W, t)
+    dot = (gh * gamma[None, :] * x).sum(axis=1)
+    gx = r[:, None] * gamma[None, :] * gh - x * (r ** 3 / H * dot)[:, None]
+    gg = (gh * x * r[:, None]).sum(axis=0)
+    return loss, gx, gg, gw
 
 
 def flce_brute(h, W, t):

@@ -6,7 +6,7 @@ It holds none of the loss head's arithmetic, so both the fp64 oracle
 """
 
 from .configs import CONFIGS, Config, config_by_name
-from .generate import Inputs, make_inputs, make_random, to_float64
+from .generate import Inputs, make_inputs, make_norm_weight, make_random, to_float64
 
 __all__ = [
     "CONFIGS",
@@ -14,6 +14,7 @@ __all__ = [
     "config_by_name",
     "Inputs",
     "make_inputs",
+    "make_norm_weight",
     "make_random",
     "to_float64",
 ]

@@ -5,7 +5,8 @@ Recipe (every step is fixed, so that every machine sees identical bits):
 * Every tensor is drawn in blocks of ``BLOCK_ROWS`` rows.  Block ``b`` of the
   tensor with tag ``T`` uses its own PCG64 stream,
   ``numpy.random.default_rng([seed, T, b])``; tags are h=1, W=2, targets=3,
-  outlier positions=4.  Blocks are independent, so they are drawn in threads.
+  outlier positions=4 (a norm weight, ``make_norm_weight``, draws on
+  ``[seed, 5]``).  Blocks are independent, so they are drawn in threads.
 * h: ``standard_normal`` in fp64.  ``rms_normal`` then divides each row by
   ``sqrt(mean(row**2) + 1e-6)`` (the output of an RMS norm with unit gain);
   ``normal_outliers`` multiplies ``round(0.001 * N * H)`` distinct entries,
@@ -150,6 +151,17 @@ def make_random(N: int, H: int, V: int, dtype: str = "bf16", seed: int = 0,
     W = _draw_blocks(seed, TAG_W, V, H, w_std, dtype)
     t = _targets(seed, N, V, targets, 1.1)
     return Inputs(h=h, W=W, t=t, dtype=dtype)
+
+
+TAG_GAMMA = 5
+
+
+def make_norm_weight(H: int, dtype: str = "bf16", seed: int = 0, std: float = 0.1) -> torch.Tensor:
+    """A norm weight [H] near 1: ``1 + std * standard_normal`` on stream
+    ``[seed, 5]``, rounded like every other input (fp64 -> fp32 -> bf16)."""
+    x = 1.0 + std * np.random.default_rng([seed, TAG_GAMMA]).standard_normal(H)
+    t = torch.from_numpy(x.astype(np.float32))
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
 
 
 def to_float64(x: torch.Tensor) -> np.ndarray:

@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
                             "flce_fwd_bwd_timed", "flce_logits", "flce_ce_rows",
                             "flce_fwd_bwd_accumulate", "flce_scale_grads",
                             "flce_cross_entropy", "flce_fwd_bwd_vocab",
-                            "flce_vocab_workspace_bytes", "flce_status_string"])
+                            "flce_vocab_workspace_bytes", "flce_fwd_bwd_rmsnorm",
+                            "flce_rmsnorm_workspace_bytes", "flce_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -221,6 +222,44 @@ def test_vocab_entry_validates(lib):
     assert _vcall(lib, dt=F32) == UNSUPPORTED
     need = lib.flce_vocab_workspace_bytes(4, 64, 128, 128, BF16)
     assert _vcall(lib, wsb=need - 1) == WORKSPACE
+
+
+def test_rmsnorm_workspace_bytes(lib):
+    f = lib.flce_rmsnorm_workspace_bytes
+    rup = lambda x: (x + 255) // 256 * 256
+    for (N, H, V, C, dt, es) in [(8192, 4096, 128256, 4096, BF16, 2), (300, 128, 1000, 128, BF16, 2),
+                                 (100, 64, 333, 33, F32, 4), (5, 8, 7, 100, BF16, 2)]:
+        base = lib.flce_workspace_bytes(N, H, V, C, dt)
+        c = min(C, N)
+        a = rup(base)
+        b = rup(a + c * H * es)
+        r = rup(b + c * H * es)
+        p = rup(r + c * 4)
+        assert f(N, H, V, C, dt) == p + (c + 63) // 64 * H * 4, (N, H, V, C)
+    assert f(0, 8, 5, 1, BF16) == 0 and f(4, 8, 5, 0, BF16) == 0
+
+
+def _rcall(lib, **kw):
+    a = dict(x=P, g=P, eps=1e-6, W=P, t=P, N=4, H=64, V=128, chunk=2, loss=P, gx=P, gg=P, gW=P,
+             ws=P, wsb=1 << 30, dt=BF16, stream=None)
+    a.update(kw)
+    return lib.flce_fwd_bwd_rmsnorm(a["x"], a["g"], ctypes.c_float(a["eps"]), a["W"], a["t"],
+                                    a["N"], a["H"], a["V"], a["chunk"], a["loss"], a["gx"],
+                                    a["gg"], a["gW"], a["ws"], a["wsb"], a["dt"], a["stream"])
+
+
+def test_rmsnorm_entry_validates(lib):
+    for field in ["x", "g", "W", "t", "loss", "gx", "gg", "gW", "ws"]:
+        assert _rcall(lib, **{field: None}) == INVALID, field
+    for field, value in [("N", 0), ("H", 0), ("V", -2), ("chunk", 0), ("dt", 9),
+                         ("eps", -1.0), ("eps", float("nan")), ("eps", float("inf"))]:
+        assert _rcall(lib, **{field: value}) == INVALID, (field, value)
+    assert _rcall(lib, H=12) == UNSUPPORTED
+    for field in ["x", "g", "gx", "gW", "ws"]:
+        assert _rcall(lib, **{field: P + 8}) == UNSUPPORTED, field
+    assert _rcall(lib, gg=P + 2) == UNSUPPORTED
+    need = lib.flce_rmsnorm_workspace_bytes(4, 64, 128, 2, BF16)
+    assert _rcall(lib, wsb=need - 1) == WORKSPACE
 
 
 def test_status_strings(lib):

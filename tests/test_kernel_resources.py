@@ -5,7 +5,8 @@ lane; a change that pushes one over makes the compiler spill to scratch
 memory, which costs HBM writes and time without changing any result.  This
 compiles each source for the device only with the compiler's resource-usage
 report and checks that the kernels of the fused path (direct-to-LDS GEMM,
-row passes, gradient scaling, fp32 GEMM) neither spill nor use scratch.
+row passes, gradient scaling, RMSNorm, fp32 GEMM) neither spill nor use
+scratch.
 The register-staged bf16 GEMM, taken only when a contraction length is not
 a multiple of 64, is compiled and reported but not held to this.
 """
@@ -23,8 +24,8 @@ CSRC = os.path.join(ROOT, "linear_cross_entropy_06_amd", "csrc")
 HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
 
 SOURCES = ["gemm_bf16_dma.hip", "gemm_bf16.hip", "gemm_f32.hip", "ce_rows.hip",
-           "grad_scale.hip", "flce_api.hip"]
-FUSED = ["gemm_bf16_dma.hip", "gemm_f32.hip", "ce_rows.hip", "grad_scale.hip"]
+           "grad_scale.hip", "rmsnorm.hip", "flce_api.hip"]
+FUSED = ["gemm_bf16_dma.hip", "gemm_f32.hip", "ce_rows.hip", "grad_scale.hip", "rmsnorm.hip"]
 
 
 def _report(src, out):
