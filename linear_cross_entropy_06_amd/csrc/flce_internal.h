@@ -53,6 +53,14 @@ struct GemmArgs {
   int64_t split_stride = 0;
 };
 
+// Whether a grid of ceil(M/bm) * ceil(N/bn) tiles (times `parts`) fits the
+// int tile indices the kernels use (launchers return hipErrorInvalidValue
+// otherwise).
+inline bool tile_count_ok(int M, int N, int bm, int bn, int parts) {
+  const int64_t t = (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn) * (parts > 1 ? parts : 1);
+  return t <= 0x7fffffff;
+}
+
 // bf16 operands, MFMA 32x32x16, fp32 accumulation.  `vec` selects the
 // 16-byte load/store path, valid when every dimension that is contiguous in
 // memory (and every leading dimension) is a multiple of 8 elements and the

@@ -329,6 +329,7 @@ using TileBig = Tile<256, 256, 64, 128, 128>;
 
 template <class T, bool A_KC, bool B_KC, bool VEC, int EPI, typename OutT>
 hipError_t launch_t(const GemmArgs& g, int m_fastest, hipStream_t s) {
+  if (!tile_count_ok(g.M, g.N, T::kBM, T::kBN, 1)) return hipErrorInvalidValue;
   const int tiles = ((g.M + T::kBM - 1) / T::kBM) * ((g.N + T::kBN - 1) / T::kBN);
   hipLaunchKernelGGL((gemm_bf16_kernel<T, A_KC, B_KC, VEC, EPI, OutT>), dim3(tiles),
                      dim3(T::NT), 0, s, g, m_fastest);

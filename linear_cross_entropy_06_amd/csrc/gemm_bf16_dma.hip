@@ -614,6 +614,7 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
   int gm = g.group_m > 0 ? g.group_m : 4;
   if (gm > tiles_m) gm = tiles_m;
   if (g.splits > 1 && !kSplitK<EPI>) return hipErrorInvalidValue;
+  if (!tile_count_ok(g.M, g.N, kBM, kBN, 1) || g.splits > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_bf16_dma_kernel<A_KC, B_KC, EPI, OutT>),
                      dim3(tiles_m * tiles_n, g.splits > 1 ? g.splits : 1), dim3(256), 0, s, g,
                      gm);

@@ -81,6 +81,7 @@ __global__ void __launch_bounds__(kNT) gemm_f32_kernel(GemmArgs g) {
 
 template <bool A_KC, bool B_KC, int EPI>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
+  if (!tile_count_ok(g.M, g.N, kBM, kBN, 1)) return hipErrorInvalidValue;
   const int tiles = ((g.M + kBM - 1) / kBM) * ((g.N + kBN - 1) / kBN);
   hipLaunchKernelGGL((gemm_f32_kernel<A_KC, B_KC, EPI>), dim3(tiles), dim3(kNT), 0, s, g);
   return hipGetLastError();

@@ -148,14 +148,17 @@ rmsnorm_bwd_kernel(const void* __restrict__ x, const void* __restrict__ gamma,
 }
 
 // part[grp][k] = sum over the rows of group grp of g_ik x_ik r_i; each
-// thread owns 4 consecutive columns, blockIdx.y is the row group.
+// thread owns 4 consecutive columns; block b covers column block
+// b % col_blocks of row group b / col_blocks.
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads)
 gamma_part_kernel(const void* __restrict__ x, const void* __restrict__ g,
-                  const float* __restrict__ rinv, int rows, int H, float* __restrict__ part) {
-  const int c4 = blockIdx.x * kThreads + threadIdx.x;
+                  const float* __restrict__ rinv, int rows, int H, int col_blocks,
+                  float* __restrict__ part) {
+  const int grp = (int)blockIdx.x / col_blocks;
+  const int c4 = ((int)blockIdx.x - grp * col_blocks) * kThreads + threadIdx.x;
   if (4 * c4 >= H) return;
-  const int i0 = blockIdx.y * kGroupRows;
+  const int i0 = grp * kGroupRows;
   const int i1 = min(rows, i0 + kGroupRows);
   float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int i = i0; i < i1; ++i) {
@@ -182,7 +185,7 @@ gamma_part_kernel(const void* __restrict__ x, const void* __restrict__ g,
 #pragma unroll
     for (int e = 0; e < 4; ++e) a[e] = __builtin_fmaf(gf[e] * xf[e], r, a[e]);
   }
-  f32x4* out = reinterpret_cast<f32x4*>(part + (int64_t)blockIdx.y * H);
+  f32x4* out = reinterpret_cast<f32x4*>(part + (int64_t)grp * H);
   out[c4] = f32x4{a[0], a[1], a[2], a[3]};
 }
 
@@ -224,18 +227,20 @@ hipError_t launch_rmsnorm_bwd(const void* x, const void* gamma, const void* g, c
       !aligned16(part))
     return hipErrorInvalidValue;
   const dim3 grid((rows + kWaves - 1) / kWaves), block(64 * kWaves);
-  const dim3 pgrid((H / 4 + kThreads - 1) / kThreads, rmsnorm_groups(rows));
+  const int col_blocks = (H / 4 + kThreads - 1) / kThreads;
+  if ((int64_t)col_blocks * rmsnorm_groups(rows) > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 pgrid(col_blocks * rmsnorm_groups(rows));
   const dim3 sgrid((H + kThreads - 1) / kThreads);
   if (bf16) {
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<true>, grid, block, 0, s, x, gamma, g, rinv, rows, H,
                        grad_x);
     hipLaunchKernelGGL(gamma_part_kernel<true>, pgrid, dim3(kThreads), 0, s, x, g, rinv, rows,
-                       H, part);
+                       H, col_blocks, part);
   } else {
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<false>, grid, block, 0, s, x, gamma, g, rinv, rows, H,
                        grad_x);
     hipLaunchKernelGGL(gamma_part_kernel<false>, pgrid, dim3(kThreads), 0, s, x, g, rinv, rows,
-                       H, part);
+                       H, col_blocks, part);
   }
   hipLaunchKernelGGL(gamma_sum_kernel, sgrid, dim3(kThreads), 0, s, part, rmsnorm_groups(rows), H,
                      grad_gamma, first);
