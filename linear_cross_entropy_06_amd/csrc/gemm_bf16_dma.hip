@@ -2,7 +2,7 @@
 //
 // Same contract as the generic kernel in gemm_bf16.hip (D[m][n] =
 // sum_k A(m,k) B(n,k), stored as out[n * ldo + m]) for the shapes the
-// loss head runs at scale: K a multiple of 32, every contiguous extent and
+// loss head runs at scale: K a multiple of 64, every contiguous extent and
 // leading dimension a multiple of 8 elements, 16-byte aligned bases.
 //
 // CDNA4 design:
@@ -36,6 +36,10 @@
 //    so the MFMAs queued before it cover the wait.
 //  * Rows beyond M/N are loaded from a clamped (valid) address and their
 //    results are never stored.
+//  * Epilogues go through LDS (each wave transposes 32 x 128 blocks in its
+//    own 16 KiB) so every store covers whole 128-byte lines; edge tests and
+//    the accumulate decision are taken once per tile, so a full tile's
+//    stores carry no branches and no per-store waits.
 #include "flce_internal.h"
 
 #include <type_traits>
