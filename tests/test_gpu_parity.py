@@ -131,6 +131,10 @@ TINY = [
     (512, 256, 768, 256, "bf16"),    # all three contractions on that kernel
     (64, 64, 40000, 64, "bf16"),     # 313 half tiles per row
     (200, 128, 1000, 1000, "bf16"),  # one 200-row chunk (not a multiple of 8)
+    (1, 64, 256, 1, "bf16"),         # a single token
+    (7, 128, 1000, 3, "bf16"),       # 3-token chunks, ragged last chunk of 1
+    (5, 64, 8, 5, "bf16"),           # one 8-column half tile
+    (64, 64, 136, 64, "bf16"),       # V = 136: second half tile holds 8 columns
     # few grad_h tiles: its K = V contraction is split in parts and summed
     (512, 256, 4096, 512, "bf16"),   # 2 tiles -> 4 parts of 16 slabs
     (1024, 512, 8192, 384, "bf16"),  # ragged 384/384/256-row chunks, 4 parts
