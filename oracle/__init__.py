@@ -20,6 +20,7 @@ from .flce_oracle import (
     rmsnorm,
     row_losses,
 )
+from .orpo_oracle import orpo, token_logp
 
 __all__ = [
     "dlogits",
@@ -31,6 +32,8 @@ __all__ = [
     "flce_vocab_chunked",
     "logits",
     "logsumexp_rows",
+    "orpo",
     "rmsnorm",
     "row_losses",
+    "token_logp",
 ]

@@ -1,0 +1,110 @@
+"""fp64 oracle of the odds-ratio preference (ORPO) loss over the same head.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/`` and never by the product
+path, with which it shares no code.
+
+What the pages fix, and what is read into them
+----------------------------------------------
+Page 2, "Liger-Kernel: Triton kernels that replace Hugging Face training
+ops", section on installation and use: the chunked post-training losses are
+called directly with the LM-head weight, the hidden states and the targets,
+and return the loss itself rather than logits; ORPO is one of them.  The
+pages give nothing more, so this module follows the published objective of
+ORPO (Hong, Lee and Thorne, "ORPO: Monolithic Preference Optimization
+without Reference Model", 2024), written out from its definition:
+
+    rows        2B sequences of T tokens; sequence s holds rows [sT, (s+1)T);
+                s < B is the chosen response of pair s, s >= B the rejected
+                response of pair s - B
+    counted     a row counts when its target is >= 0 (a negative target
+                marks a prompt or padding position)
+    log p_r     = Z[r, t_r] - lse_r,  Z = h W^T             (per counted row)
+    l_s         = mean of log p_r over the counted rows of sequence s
+    logodds_s   = l_s - ln(1 - exp(l_s))
+    L_OR        = -(1/B) sum_b ln sigmoid(logodds_b - logodds_{B+b})
+    L_SFT       = -(1/M) sum of log p_r over the counted chosen rows
+                  (M of them in the whole batch)
+    loss        = L_SFT + beta * L_OR
+
+Gradient: with c_r = -dloss/dlog p_r (zero for rows that do not count),
+dloss/dZ[r, :] = c_r (softmax(Z_r) - onehot(t_r)); grad_h = G W and
+grad_W = G^T h as for the plain head.  By the chain rule, for a counted row
+of pair b,
+
+    c_r = 1/M [chosen only] + beta/B * sigmoid(-(lo_b - lo_{B+b}))
+          * (+1 chosen, -1 rejected) / ((1 - exp(l_s)) n_s)
+
+with n_s the counted rows of the row's sequence s.  A sequence with no
+counted row has no mean log-probability; the result is then NaN.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _split(t: np.ndarray, pairs: int, seq_len: int):
+    t = np.asarray(t)
+    if t.shape != (2 * pairs * seq_len,):
+        raise ValueError("targets must hold 2 * pairs * seq_len rows")
+    return t.reshape(2 * pairs, seq_len)
+
+
+def token_logp(h: np.ndarray, W: np.ndarray, t: np.ndarray):
+    """log softmax(h W^T)[r, t_r] for counted rows (0 elsewhere), the softmax
+    P and the counted mask, all fp64."""
+    h = np.asarray(h, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    t = np.asarray(t)
+    V = W.shape[0]
+    if np.any(t >= V):
+        raise ValueError("target >= V")
+    Z = h @ W.T
+    m = Z.max(axis=1, keepdims=True)
+    lse = (m + np.log(np.exp(Z - m).sum(axis=1, keepdims=True)))[:, 0]
+    P = np.exp(Z - lse[:, None])
+    counted = t >= 0
+    logp = np.zeros(h.shape[0])
+    rows = np.nonzero(counted)[0]
+    logp[rows] = Z[rows, t[rows]] - lse[rows]
+    return logp, P, counted
+
+
+def orpo(h, W, t, pairs: int, seq_len: int, beta: float):
+    """ORPO loss and gradients; returns (loss, grad_h, grad_W, seq_logp)
+    with seq_logp[s] the mean log-probability l_s of sequence s."""
+    h = np.asarray(h, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    t = np.asarray(t)
+    B, T = pairs, seq_len
+    _split(t, B, T)
+    logp, P, counted = token_logp(h, W, t)
+    lp = logp.reshape(2 * B, T)
+    cnt = counted.reshape(2 * B, T).sum(axis=1).astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        l_seq = lp.sum(axis=1) / cnt                     # mean log p per sequence
+        logodds = l_seq - np.log1p(-np.exp(l_seq))       # ln(P / (1 - P))
+    ratio = logodds[:B] - logodds[B:]
+    # -ln sigmoid(x) = ln(1 + exp(-x)), written stably
+    with np.errstate(invalid="ignore"):
+        l_or = float(np.mean(np.logaddexp(0.0, -ratio)))
+    M = float(counted[: B * T].sum())
+    l_sft = float(-logp[: B * T].sum() / M) if M > 0 else math.nan
+    loss = l_sft + beta * l_or
+
+    # c_r = -dloss/dlog p_r
+    sig_neg = 1.0 / (1.0 + np.exp(ratio))                # sigmoid(-ratio)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        per_seq = beta / B * np.concatenate([sig_neg, -sig_neg]) / (
+            (1.0 - np.exp(l_seq)) * cnt)
+    c = np.repeat(per_seq, T)
+    c[: B * T] += 1.0 / M if M > 0 else math.nan
+    c = np.where(counted, c, 0.0)
+    G = P.copy()
+    rows = np.nonzero(counted)[0]
+    G[rows, t[rows]] -= 1.0
+    G *= c[:, None]
+    return loss, G @ W, G.T @ h, l_seq
+
