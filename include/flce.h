@@ -291,6 +291,61 @@ flce_status flce_fwd_bwd_vocab(const void* h, const void* W, const int32_t* targ
 size_t flce_vocab_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t vchunk,
                                   flce_dtype dt);
 
+/*
+ * Odds-ratio preference (ORPO) loss over the same head.  Page 2,
+ * "Liger-Kernel: Triton kernels that replace Hugging Face training ops",
+ * section on installation and use, lists ORPO among the chunked
+ * post-training losses called with the LM-head weight, the hidden states
+ * and the targets that return the loss itself; the pages give no formula,
+ * so the objective is the published one of ORPO (Hong, Lee and Thorne,
+ * 2024):
+ *   rows       N = 2 * pairs * seq_len rows of h [N, H] and targets [N]:
+ *              sequence s = row / seq_len; sequences [0, pairs) are the
+ *              chosen responses, [pairs, 2 pairs) the rejected ones, pair b
+ *              = (b, pairs + b)
+ *   counted    a row counts when its target is >= 0; a negative target
+ *              marks a prompt or padding row (no loss, zero gradient row)
+ *   l_s        mean of log softmax(h_r W^T)[t_r] over the counted rows of s
+ *   loss       -(1/M) sum over counted chosen rows of log p
+ *              + beta * (1/pairs) sum_b ln(1 + exp(-(lo_b - lo_{pairs+b})))
+ *              with lo_s = l_s - ln(1 - exp(l_s)) and M the counted chosen
+ *              rows of the batch
+ * Outputs (overwritten): *loss; seq_logp[2 pairs] = l_s (optional, may be
+ * NULL); grad_h [N, H] bf16 = dloss/dh; grad_W [V, H] fp32 = dloss/dW.
+ * The batch is processed in chunks of min(chunk_pairs, pairs) pairs, each
+ * pair's two sequences in the same chunk; the logits of one chunk are the
+ * only [rows, V] array.  A sequence with no counted row, or a target >= V,
+ * makes the loss NaN (targets are never read on the host).
+ * Supported: FLCE_BF16 with H % 64 == 0, V % 8 == 0 and H below 2^22;
+ * otherwise FLCE_ERR_UNSUPPORTED.  FLCE_ERR_INVALID_ARG for a null required
+ * pointer, pairs, seq_len or chunk_pairs < 1, more than 2^31 - 1 rows, or a
+ * beta that is not finite.  Alignment, workspace and stream rules as
+ * flce_fwd_bwd (seq_logp 4-byte aligned).
+ */
+flce_status flce_orpo_fwd_bwd(const void* h, const void* W, const int32_t* targets,
+                              int64_t pairs, int64_t seq_len, int64_t H, int64_t V,
+                              int64_t chunk_pairs, float beta, float* loss, float* seq_logp,
+                              void* grad_h, float* grad_W, void* workspace,
+                              size_t workspace_bytes, flce_dtype dt, hipStream_t stream);
+
+/*
+ * Bytes of device workspace flce_orpo_fwd_bwd needs, with R = 2 * Pc *
+ * seq_len rows per chunk (Pc = min(chunk_pairs, pairs)), each region
+ * rounded up to 256 bytes:
+ *   R * V * 2             bf16 logits of one chunk
+ * + R * ceil(V/128) * 8   (max, sum) per row and 128-column slice
+ * + K-split rows * H * 4  fp32 grad_h parts when a chunk has few H x R tiles
+ * + R * 16                per-row log-sum-exp, target logit, loss and scale
+ * + 2 * R * H * 2         the chunk's h rows and grad_h rows
+ * + R * 4                 the chunk's targets
+ * + pairs * 8             per-pair loss terms
+ * + 256                   the count of counted chosen rows
+ * Returns 0 when an argument is invalid or the shape unsupported.  Pure
+ * host function.
+ */
+size_t flce_orpo_workspace_bytes(int64_t pairs, int64_t seq_len, int64_t H, int64_t V,
+                                 int64_t chunk_pairs, flce_dtype dt);
+
 /* A static, human-readable name for a status code (host only). */
 const char* flce_status_string(flce_status s);
 

@@ -44,6 +44,8 @@ EXPORTS = (
     "flce_vocab_workspace_bytes",
     "flce_fwd_bwd_rmsnorm",
     "flce_rmsnorm_workspace_bytes",
+    "flce_orpo_fwd_bwd",
+    "flce_orpo_workspace_bytes",
     "flce_status_string",
 )
 
@@ -100,6 +102,11 @@ def load() -> ctypes.CDLL:
     lib.flce_fwd_bwd_rmsnorm.restype = ctypes.c_int
     lib.flce_rmsnorm_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.flce_rmsnorm_workspace_bytes.restype = sz
+    lib.flce_orpo_fwd_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp,
+                                      vp, vp, vp, vp, sz, ctypes.c_int, vp]
+    lib.flce_orpo_fwd_bwd.restype = ctypes.c_int
+    lib.flce_orpo_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int]
+    lib.flce_orpo_workspace_bytes.restype = sz
     lib.flce_status_string.argtypes = [ctypes.c_int]
     lib.flce_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -324,6 +331,60 @@ def fwd_bwd_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, W: torch.Tensor,
                                   _stream_ptr(dev))
     _check(st)
     return loss, grad_x, grad_gamma, grad_W
+
+
+def orpo_workspace_bytes(pairs: int, seq_len: int, H: int, V: int, chunk_pairs: int,
+                         dtype: torch.dtype) -> int:
+    """Workspace of ``flce_orpo_fwd_bwd`` (0 when the shape is unsupported)."""
+    dt = FLCE_BF16 if dtype == torch.bfloat16 else FLCE_F32
+    return int(load().flce_orpo_workspace_bytes(pairs, seq_len, H, V, chunk_pairs, dt))
+
+
+def orpo_fwd_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, pairs: int,
+                 seq_len: int, beta: float = 0.1, chunk_pairs: Optional[int] = None, *,
+                 loss: Optional[torch.Tensor] = None,
+                 seq_logp: Optional[torch.Tensor] = None,
+                 grad_h: Optional[torch.Tensor] = None,
+                 grad_W: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None,
+                 ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Odds-ratio preference loss via ``flce_orpo_fwd_bwd``: rows of h and
+    targets are 2 * pairs sequences of seq_len tokens, the chosen responses
+    first; a negative target marks a row that does not count.  Returns
+    (loss [] fp32, seq_logp [2 pairs] fp32, grad_h like h, grad_W [V, H] fp32)."""
+    lib = load()
+    _need_cuda(h, W, targets)
+    if targets.dtype != torch.int32:
+        raise TypeError("targets must be int32")
+    if W.dtype != h.dtype:
+        raise TypeError("h and W must share a dtype")
+    N, H = h.shape
+    V = W.shape[0]
+    if N != 2 * pairs * seq_len or targets.shape != (N,):
+        raise ValueError("h and targets must hold 2 * pairs * seq_len rows")
+    chunk_pairs = pairs if chunk_pairs is None else int(chunk_pairs)
+    dt = _dt(h)
+    dev = h.device
+    if loss is None:
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+    if seq_logp is None:
+        seq_logp = torch.empty(2 * pairs, dtype=torch.float32, device=dev)
+    if grad_h is None:
+        grad_h = torch.empty_like(h)
+    if grad_W is None:
+        grad_W = torch.empty((V, H), dtype=torch.float32, device=dev)
+    need = int(lib.flce_orpo_workspace_bytes(pairs, seq_len, H, V, chunk_pairs, dt))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need_cuda(loss, seq_logp, grad_h, grad_W, workspace)
+    st = lib.flce_orpo_fwd_bwd(h.data_ptr(), W.data_ptr(), targets.data_ptr(), pairs, seq_len,
+                               H, V, chunk_pairs, float(beta), loss.data_ptr(),
+                               seq_logp.data_ptr(), grad_h.data_ptr(), grad_W.data_ptr(),
+                               workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), dt,
+                               _stream_ptr(dev))
+    _check(st)
+    return loss, seq_logp, grad_h, grad_W
 
 
 def logits(h: torch.Tensor, W: torch.Tensor, z: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -245,12 +245,12 @@ __device__ __forceinline__ float target_logit(const uint16_t* h_row, const uint1
   return acc;
 }
 
-// u -> u * 2^(mx_q - shift) over n elements of a row (n % 8 == 0), in
-// place, 8 elements (one slice of a half tile) per lane and step; pr holds
-// the row's (max, sum) pairs from the row's first element on.
+// u -> sign * u * 2^(mx_q - shift) over n elements of a row (n % 8 == 0),
+// in place, 8 elements (one slice of a half tile) per lane and step; pr
+// holds the row's (max, sum) pairs from the row's first element on.
 template <int UNROLL>
 __device__ __forceinline__ void rescale_row(uint16_t* ur, const float* pr, int n, float shift,
-                                            int lane) {
+                                            int lane, float sign = 1.0f) {
   u32x4* uv = reinterpret_cast<u32x4*>(ur);
   const int nvec = n >> 3;
   for (int v0 = 0; v0 < nvec; v0 += 64 * UNROLL) {
@@ -268,7 +268,7 @@ __device__ __forceinline__ void rescale_row(uint16_t* ur, const float* pr, int n
     for (int k = 0; k < UNROLL; ++k) {
       const int v = v0 + lane + 64 * k;
       if (v >= nvec) continue;
-      const float c = exp2_hw(f[k] - shift);
+      const float c = exp2_hw(f[k] - shift) * sign;
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(bf16_lo(x[k][e]) * c, bf16_hi(x[k][e]) * c);
@@ -339,18 +339,27 @@ ce_stats_exp_kernel(const float* __restrict__ row_part, int64_t ldp,
 // Vocabulary-chunked gradient of one chunk of columns [v0, v0 + n): u -> G
 // in place with the rows' lse2 from every chunk, and the target's element
 // (when it falls in the chunk) rewritten as (2^(zt2 - lse2) - 1) * scale.
+// With row_scale, row i takes the scale row_scale[i] instead (any sign; 0
+// clears the row) and a negative target leaves no one-hot element.
 template <int UNROLL>
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
 ce_rewrite_exp_kernel(uint16_t* __restrict__ u, int64_t ldu, const float* __restrict__ row_part,
                       int64_t ldp, const float* __restrict__ lse2_in,
                       const float* __restrict__ zt2_in, const int32_t* __restrict__ targets,
-                      int rows, int v0, int n, float scale) {
+                      int rows, int v0, int n, float scale, const float* __restrict__ row_scale) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
   const float lse2 = lse2_in[row];
   uint16_t* ur = u + (int64_t)row * ldu;
-  rescale_row<UNROLL>(ur, row_part + (int64_t)row * ldp, n, lse2 - log2_hw(scale), lane);
+  float sign = 1.0f;
+  if (row_scale) {
+    scale = row_scale[row];
+    sign = scale < 0.0f ? -1.0f : 1.0f;
+  }
+  // |scale| folds into the exponent (log2 0 = -inf clears the row).
+  rescale_row<UNROLL>(ur, row_part + (int64_t)row * ldp, n,
+                      lse2 - log2_hw(__builtin_fabsf(scale)), lane, sign);
   const int t = targets[row] - v0;
   if (t >= 0 && t < n && lane == 0) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -533,7 +542,8 @@ hipError_t launch_ce_stats_exp(const float* row_part, int64_t ldp, const uint16_
 
 hipError_t launch_ce_rewrite_exp(uint16_t* u, int64_t ldu, const float* row_part, int64_t ldp,
                                  const float* lse2, const float* zt2, const int32_t* targets,
-                                 int rows, int v0, int n, float scale, hipStream_t s) {
+                                 int rows, int v0, int n, float scale, const float* row_scale,
+                                 hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   // 16-byte pieces of u rows; the chunk starts on a half tile.
   if ((n % 8) || (v0 % kHalfTile) || (ldu % 8) || (reinterpret_cast<uintptr_t>(u) & 15) ||
@@ -541,7 +551,7 @@ hipError_t launch_ce_rewrite_exp(uint16_t* u, int64_t ldu, const float* row_part
     return hipErrorInvalidValue;
   hipLaunchKernelGGL((ce_rewrite_exp_kernel<4>), dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock),
                      dim3(64 * kWavesPerBlock), 0, s, u, ldu, row_part, ldp, lse2, zt2, targets,
-                     rows, v0, n, scale);
+                     rows, v0, n, scale, row_scale);
   return hipGetLastError();
 }
 

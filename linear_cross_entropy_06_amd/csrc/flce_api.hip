@@ -547,7 +547,7 @@ extern "C" flce_status flce_fwd_bwd_vocab(const void* h, const void* W, const in
     if (logits(v0, n) != hipSuccess) return FLCE_ERR_HIP;
     if (flce::launch_ce_rewrite_exp(u, Vc, pairs + 2 * (v0 / flce::kHalfTile), ldp, lse2, zt2,
                                     targets, rows, static_cast<int>(v0), static_cast<int>(n),
-                                    inv_n, stream) != hipSuccess)
+                                    inv_n, nullptr, stream) != hipSuccess)
       return FLCE_ERR_HIP;
     // grad_h^T (+)= W_c^T . G^T: A(m = hidden, k = vocab) = W[v0 + k][m],
     // B(n = token, k = vocab) = G[n][k]; fp32, accumulated after chunk 0.
@@ -567,6 +567,185 @@ extern "C" flce_status flce_fwd_bwd_vocab(const void* h, const void* W, const in
   }
   return flce::launch_sum_parts_bf16(gacc, 1, N * H, static_cast<uint16_t*>(grad_h), N * H,
                                      stream) == hipSuccess
+             ? FLCE_OK
+             : FLCE_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Odds-ratio preference loss over the same head (page 2, "Liger-Kernel:
+// Triton kernels that replace Hugging Face training ops", section on
+// installation and use: ORPO is one of the chunked post-training losses
+// called with the LM-head weight, the hidden states and the targets; the
+// objective is the published one, see orpo.hip).  Rows: 2B sequences of T
+// tokens, sequences [0, B) chosen, [B, 2B) rejected.  The batch is worked
+// through in chunks of Pc pairs; a chunk's chosen and rejected rows are
+// copied next to each other into the workspace, so every pair's two
+// sequences are in one chunk and the head's kernels run unchanged:
+//   0. count of counted chosen rows (once)
+//   1. h_c, t_c  <- the chunk's chosen rows, then its rejected rows
+//   2. exponentiated logits and (max, sum) pairs of h_c           MFMA
+//   3. per row lse2 and log2 of the target logit
+//   4. per pair: mean log-probabilities, log odds, the loss terms; per row
+//      the gradient scale c = -dloss/dlog p
+//   5. u -> G = c (softmax - onehot) in place
+//   6. grad_h_c = G W, copied back to the chunk's rows of grad_h     MFMA
+//   7. grad_W (+)= G^T h_c                                           MFMA
+// and finally the loss from the staged per-pair terms.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct OrpoLayout {
+  int64_t pairs, parts, stats, hc, ghc, tc, stage, count, total;
+};
+inline OrpoLayout orpo_layout(int64_t B, int64_t T, int64_t Pc, int64_t H, int64_t V) {
+  const int64_t R = 2 * Pc * T;        // rows of a full chunk
+  const int64_t Rl = 2 * (B % Pc) * T; // rows of a shorter last chunk (0: none)
+  int64_t split_rows = 0;
+  for (int64_t r : {R, Rl}) {
+    if (r <= 0) continue;
+    const int sp = grad_h_splits(H, r, V);
+    if (sp > 1 && sp * r > split_rows) split_rows = sp * r;
+  }
+  OrpoLayout l;
+  l.pairs = round_up(R * V * 2, 256);                             // u [R][V] bf16
+  l.parts = round_up(l.pairs + R * n_half_tiles(V) * 8, 256);     // (max, sum) pairs
+  l.stats = round_up(l.parts + split_rows * H * 4, 256);          // grad_h K-split parts
+  l.hc = round_up(l.stats + 4 * R * 4, 256);                      // lse2, zt2, loss, coef
+  l.ghc = round_up(l.hc + R * H * 2, 256);                        // h_c [R][H] bf16
+  l.tc = round_up(l.ghc + R * H * 2, 256);                        // grad_h_c [R][H] bf16
+  l.stage = round_up(l.tc + R * 4, 256);                          // t_c [R]
+  l.count = round_up(l.stage + 2 * B * 4, 256);                   // per-pair terms [B][2]
+  l.total = l.count + 256;                                        // counted chosen rows
+  return l;
+}
+
+// Sizes the preference loss runs: bf16 on the exponentiated-logits path,
+// int-sized row counts.
+inline bool orpo_args_ok(int64_t B, int64_t T, int64_t H, int64_t V, int64_t Pc,
+                         flce_dtype dt) {
+  if (B < 1 || T < 1 || Pc < 1 || !dims_ok(H) || !dims_ok(V) || !dtype_ok(dt)) return false;
+  if (B > kMaxDim / 2 || T > kMaxDim / (2 * B)) return false;  // 2 B T rows fit an int
+  return true;
+}
+
+}  // namespace
+
+extern "C" size_t flce_orpo_workspace_bytes(int64_t pairs, int64_t seq_len, int64_t H,
+                                            int64_t V, int64_t chunk_pairs, flce_dtype dt) {
+  if (!orpo_args_ok(pairs, seq_len, H, V, chunk_pairs, dt) || !exp_path(H, V, dt)) return 0;
+  const int64_t Pc = chunk_pairs < pairs ? chunk_pairs : pairs;
+  return static_cast<size_t>(orpo_layout(pairs, seq_len, Pc, H, V).total);
+}
+
+extern "C" flce_status flce_orpo_fwd_bwd(const void* h, const void* W, const int32_t* targets,
+                                         int64_t pairs, int64_t seq_len, int64_t H, int64_t V,
+                                         int64_t chunk_pairs, float beta, float* loss,
+                                         float* seq_logp, void* grad_h, float* grad_W,
+                                         void* workspace, size_t workspace_bytes,
+                                         flce_dtype dt, hipStream_t stream) {
+  if (!h || !W || !targets || !loss || !grad_h || !grad_W || !workspace)
+    return FLCE_ERR_INVALID_ARG;
+  if (!orpo_args_ok(pairs, seq_len, H, V, chunk_pairs, dt)) return FLCE_ERR_INVALID_ARG;
+  if (!(beta == beta) || beta > 3.0e38f || beta < -3.0e38f) return FLCE_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(W) || !aligned16(grad_h) || !aligned16(grad_W) ||
+      !aligned16(workspace) || (reinterpret_cast<uintptr_t>(targets) & 3u) ||
+      (reinterpret_cast<uintptr_t>(loss) & 3u) || (reinterpret_cast<uintptr_t>(seq_logp) & 3u))
+    return FLCE_ERR_UNSUPPORTED;
+  if (!exp_path(H, V, dt)) return FLCE_ERR_UNSUPPORTED;
+  if (workspace_bytes < flce_orpo_workspace_bytes(pairs, seq_len, H, V, chunk_pairs, dt))
+    return FLCE_ERR_WORKSPACE;
+
+  const int64_t B = pairs, T = seq_len;
+  const int64_t Pc = chunk_pairs < B ? chunk_pairs : B;
+  const OrpoLayout lay = orpo_layout(B, T, Pc, H, V);
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* u = reinterpret_cast<uint16_t*>(ws);
+  float* rpairs = reinterpret_cast<float*>(ws + lay.pairs);
+  float* parts = reinterpret_cast<float*>(ws + lay.parts);
+  const int64_t R = 2 * Pc * T;
+  float* lse2 = reinterpret_cast<float*>(ws + lay.stats);
+  float* zt2 = lse2 + R;
+  float* row_loss = zt2 + R;
+  float* coef = row_loss + R;
+  uint16_t* hc = reinterpret_cast<uint16_t*>(ws + lay.hc);
+  uint16_t* ghc = reinterpret_cast<uint16_t*>(ws + lay.ghc);
+  int32_t* tc = reinterpret_cast<int32_t*>(ws + lay.tc);
+  float* stage = reinterpret_cast<float*>(ws + lay.stage);
+  int* count = reinterpret_cast<int*>(ws + lay.count);
+  const int64_t ldp = 2 * n_half_tiles(V);
+  const uint16_t* h16 = static_cast<const uint16_t*>(h);
+  const uint16_t* W16 = static_cast<const uint16_t*>(W);
+  uint16_t* gh16 = static_cast<uint16_t*>(grad_h);
+  const hipMemcpyKind d2d = hipMemcpyDeviceToDevice;
+
+  // 0. counted chosen rows over the whole batch (the SFT term's mean).
+  if (flce::launch_orpo_count(targets, B * T, count, stream) != hipSuccess) return FLCE_ERR_HIP;
+
+  for (int64_t p0 = 0; p0 < B; p0 += Pc) {
+    const int64_t pc = (B - p0) < Pc ? (B - p0) : Pc;
+    const int64_t half = pc * T;  // chosen rows of the chunk (as many rejected)
+    const int rows = static_cast<int>(2 * half);
+    const int64_t cw = p0 * T, cr = (B + p0) * T;  // first chosen / rejected row in the batch
+
+    // 1. stage the chunk's rows contiguously.
+    if (hipMemcpyAsync(hc, h16 + cw * H, half * H * 2, d2d, stream) != hipSuccess ||
+        hipMemcpyAsync(hc + half * H, h16 + cr * H, half * H * 2, d2d, stream) != hipSuccess ||
+        hipMemcpyAsync(tc, targets + cw, half * 4, d2d, stream) != hipSuccess ||
+        hipMemcpyAsync(tc + half, targets + cr, half * 4, d2d, stream) != hipSuccess)
+      return FLCE_ERR_HIP;
+
+    // 2. exponentiated logits of h_c and their (max, sum) pairs.
+    flce::GemmArgs g1{W, H, hc, H, u, V, static_cast<int>(V), rows, static_cast<int>(H), 0};
+    g1.group_m = 4;
+    g1.stagger = 37;
+    g1.row_part = rpairs;
+    g1.ldp = ldp;
+    if (flce::launch_gemm_bf16(true, true, flce::kExpBF16, true, g1, stream) != hipSuccess)
+      return FLCE_ERR_HIP;
+
+    // 3.-5. row statistics, per-pair terms and row scales, G in place.
+    if (flce::launch_ce_stats_exp(rpairs, ldp, hc, W16, static_cast<int>(H), tc, rows,
+                                  static_cast<int>(V), lse2, zt2, row_loss, stream) !=
+            hipSuccess ||
+        flce::launch_orpo_coef(lse2, zt2, tc, static_cast<int>(pc), static_cast<int>(T),
+                               static_cast<int>(B), static_cast<int>(p0), beta, count, coef,
+                               seq_logp, stage, stream) != hipSuccess ||
+        flce::launch_ce_rewrite_exp(u, V, rpairs, ldp, lse2, zt2, tc, rows, 0,
+                                    static_cast<int>(V), 1.0f, coef, stream) != hipSuccess)
+      return FLCE_ERR_HIP;
+
+    // 6. grad_h_c^T = W^T . G^T (K split for few output tiles), then back
+    //    to the chunk's rows of grad_h.
+    flce::GemmArgs g4{W, H, u, V, ghc, H, static_cast<int>(H), rows, static_cast<int>(V), 0};
+    g4.group_m = 4;
+    const int splits = grad_h_splits(H, rows, V);
+    hipError_t e;
+    if (splits > 1) {
+      g4.out = parts;
+      g4.splits = splits;
+      g4.split_stride = static_cast<int64_t>(rows) * H;
+      e = flce::launch_gemm_bf16(false, true, flce::kStoreF32, true, g4, stream);
+      if (e == hipSuccess)
+        e = flce::launch_sum_parts_bf16(parts, splits, static_cast<int64_t>(rows) * H, ghc,
+                                        static_cast<int64_t>(rows) * H, stream);
+    } else {
+      e = flce::launch_gemm_bf16(false, true, flce::kStoreOut, true, g4, stream);
+    }
+    if (e != hipSuccess ||
+        hipMemcpyAsync(gh16 + cw * H, ghc, half * H * 2, d2d, stream) != hipSuccess ||
+        hipMemcpyAsync(gh16 + cr * H, ghc + half * H, half * H * 2, d2d, stream) != hipSuccess)
+      return FLCE_ERR_HIP;
+
+    // 7. grad_W^T (+)= h_c^T . G.
+    flce::GemmArgs g5{hc, H, u, V, grad_W, H, static_cast<int>(H), static_cast<int>(V), rows,
+                      p0 == 0 ? 0 : 1};
+    g5.group_m = 4;
+    g5.stagger = 37;
+    if (flce::launch_gemm_bf16(false, false, flce::kAccumF32, true, g5, stream) != hipSuccess)
+      return FLCE_ERR_HIP;
+  }
+  return flce::launch_orpo_loss(stage, static_cast<int>(B), beta, count, loss, stream) ==
+                 hipSuccess
              ? FLCE_OK
              : FLCE_ERR_HIP;
 }

@@ -113,10 +113,32 @@ hipError_t launch_ce_stats_exp(const float* row_part, int64_t ldp, const uint16_
                                float* lse2, float* zt2, float* row_loss, hipStream_t s);
 // Vocabulary-chunked path, gradient of columns [v0, v0 + n) (v0 % 128 == 0,
 // n % 8 == 0): u (row pitch ldu) -> (u 2^(mx_q - lse2) - [j == t]) * scale
-// in place; row_part points at the chunk's first pair of row 0.
+// in place; row_part points at the chunk's first pair of row 0.  A non-null
+// row_scale gives each row its own scale (any sign) in place of `scale`.
 hipError_t launch_ce_rewrite_exp(uint16_t* u, int64_t ldu, const float* row_part, int64_t ldp,
                                  const float* lse2, const float* zt2, const int32_t* targets,
-                                 int rows, int v0, int n, float scale, hipStream_t s);
+                                 int rows, int v0, int n, float scale, const float* row_scale,
+                                 hipStream_t s);
+
+// Odds-ratio preference loss (orpo.hip).  Rows of a batch of 2B sequences of
+// T tokens: sequences [0, B) chosen, [B, 2B) rejected; a negative target
+// marks a row that does not count.
+//   orpo_count: *count = number of rows r < n with targets[r] >= 0.
+//   orpo_coef:  for the Pc pairs [p0, p0 + Pc) staged as one chunk (chosen
+//     rows [0, Pc T), rejected rows [Pc T, 2 Pc T), with lse2 / zt2 of each
+//     row from launch_ce_stats_exp): each row's gradient scale
+//     c = -dloss/dlog p (0 for rows that do not count) into coef, each
+//     sequence's mean log-probability into seq_logp[p] and seq_logp[B + p]
+//     (when non-null), and per pair the chosen rows' -sum log p and the
+//     odds-ratio term ln(1 + exp(-ratio)) into stage[2p], stage[2p + 1].
+//   orpo_loss:  *loss = sum_p stage[2p] / count + beta / B sum_p stage[2p+1],
+//     fixed-order fp64 sums.
+hipError_t launch_orpo_count(const int32_t* targets, int64_t n, int* count, hipStream_t s);
+hipError_t launch_orpo_coef(const float* lse2, const float* zt2, const int32_t* targets, int Pc,
+                            int T, int B, int p0, float beta, const int* count, float* coef,
+                            float* seq_logp, float* stage, hipStream_t s);
+hipError_t launch_orpo_loss(const float* stage, int B, float beta, const int* count, float* loss,
+                            hipStream_t s);
 
 // RMSNorm in front of the head (rmsnorm.hip), one wave per row, H % 8 == 0,
 // 16-byte aligned rows: h = x * r * gamma with r = 1/sqrt(mean x^2 + eps)

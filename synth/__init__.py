@@ -6,15 +6,18 @@ It holds none of the loss head's arithmetic, so both the fp64 oracle
 """
 
 from .configs import CONFIGS, Config, config_by_name
-from .generate import Inputs, make_inputs, make_norm_weight, make_random, to_float64
+from .generate import (IGNORE, Inputs, make_inputs, make_norm_weight, make_random,
+                       mask_preference_rows, to_float64)
 
 __all__ = [
     "CONFIGS",
     "Config",
+    "IGNORE",
     "config_by_name",
     "Inputs",
     "make_inputs",
     "make_norm_weight",
     "make_random",
+    "mask_preference_rows",
     "to_float64",
 ]

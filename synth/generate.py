@@ -6,7 +6,8 @@ Recipe (every step is fixed, so that every machine sees identical bits):
   tensor with tag ``T`` uses its own PCG64 stream,
   ``numpy.random.default_rng([seed, T, b])``; tags are h=1, W=2, targets=3,
   outlier positions=4 (a norm weight, ``make_norm_weight``, draws on
-  ``[seed, 5]``).  Blocks are independent, so they are drawn in threads.
+  ``[seed, 5]``; the prompt and padding lengths of a preference batch,
+  ``mask_preference_rows``, on ``[seed, 6]``).  Blocks are independent, so they are drawn in threads.
 * h: ``standard_normal`` in fp64.  ``rms_normal`` then divides each row by
   ``sqrt(mean(row**2) + 1e-6)`` (the output of an RMS norm with unit gain);
   ``normal_outliers`` multiplies ``round(0.001 * N * H)`` distinct entries,
@@ -167,3 +168,32 @@ def make_norm_weight(H: int, dtype: str = "bf16", seed: int = 0, std: float = 0.
 def to_float64(x: torch.Tensor) -> np.ndarray:
     """Exact upcast of stored bf16/fp32 values to fp64 numpy."""
     return x.detach().to("cpu").to(torch.float64).numpy()
+
+
+TAG_MASK = 6
+IGNORE = -100
+
+
+def mask_preference_rows(t: torch.Tensor, pairs: int, seq_len: int, seed: int = 0,
+                         prompt_max: int = 0, pad_max: int = 0) -> torch.Tensor:
+    """Targets of a preference batch (2 * pairs sequences of seq_len rows,
+    chosen responses first) with prompt and padding rows marked IGNORE.
+
+    On stream ``[seed, 6]``: per pair a prompt length ``integers(0,
+    prompt_max + 1)`` shared by its two sequences, then per sequence (chosen
+    of every pair, then rejected) a padding length ``integers(0, pad_max +
+    1)``; both are cut so that every sequence keeps at least one row.  The
+    first prompt-length rows and the last padding-length rows of each
+    sequence become IGNORE."""
+    rng = np.random.default_rng([seed, TAG_MASK])
+    prompt = rng.integers(0, prompt_max + 1, pairs)
+    pad = rng.integers(0, pad_max + 1, 2 * pairs)
+    out = t.clone()
+    v = out.view(2 * pairs, seq_len)
+    for s in range(2 * pairs):
+        a = min(int(prompt[s % pairs]), seq_len - 1)
+        b = min(int(pad[s]), seq_len - 1 - a)
+        v[s, :a] = IGNORE
+        if b > 0:
+            v[s, seq_len - b:] = IGNORE
+    return out

@@ -41,7 +41,8 @@ def test_header_declares_the_boundary():
                             "flce_fwd_bwd_accumulate", "flce_scale_grads",
                             "flce_cross_entropy", "flce_fwd_bwd_vocab",
                             "flce_vocab_workspace_bytes", "flce_fwd_bwd_rmsnorm",
-                            "flce_rmsnorm_workspace_bytes", "flce_status_string"])
+                            "flce_rmsnorm_workspace_bytes", "flce_orpo_fwd_bwd",
+                            "flce_orpo_workspace_bytes", "flce_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -260,6 +261,67 @@ def test_rmsnorm_entry_validates(lib):
     assert _rcall(lib, gg=P + 2) == UNSUPPORTED
     need = lib.flce_rmsnorm_workspace_bytes(4, 64, 128, 2, BF16)
     assert _rcall(lib, wsb=need - 1) == WORKSPACE
+
+
+def test_orpo_workspace_bytes(lib):
+    f = lib.flce_orpo_workspace_bytes
+    rup = lambda x: (x + 255) // 256 * 256
+
+    def splits(H, rows, V):
+        tiles = ((H + 255) // 256) * ((rows + 255) // 256)
+        s = 4 if tiles <= 64 else 2 if tiles <= 128 else 1
+        return s if (V % 64 == 0 and V // 64 >= 16 * s) else 1
+
+    def formula(B, T, H, V, cp):
+        pc = min(cp, B)
+        R, Rl = 2 * pc * T, 2 * (B % pc) * T
+        sr = max([splits(H, r, V) * r for r in (R, Rl) if r > 0 and splits(H, r, V) > 1],
+                 default=0)
+        a = rup(R * V * 2)
+        b = rup(a + R * ((V + 127) // 128) * 8)
+        c = rup(b + sr * H * 4)
+        d = rup(c + 4 * R * 4)
+        e = rup(d + R * H * 2)
+        g = rup(e + R * H * 2)
+        st = rup(g + R * 4)
+        cnt = rup(st + 2 * B * 4)
+        return cnt + 256
+
+    for args in [(4, 1024, 4096, 128256, 2), (2, 512, 4096, 32000, 1), (3, 100, 128, 1000, 2),
+                 (5, 7, 64, 8, 10), (1, 1, 64, 256, 1)]:
+        assert f(*args, BF16) == formula(*args), args
+    for bad in [(2, 8, 72, 256, 1, BF16),    # H % 64
+                (2, 8, 64, 100, 1, BF16),    # V % 8
+                (2, 8, 64, 256, 1, F32),     # dtype
+                (0, 8, 64, 256, 1, BF16), (2, 0, 64, 256, 1, BF16), (2, 8, 64, 256, 0, BF16),
+                (2 ** 30, 4, 64, 256, 1, BF16)]:   # more than 2^31 - 1 rows
+        assert f(*bad) == 0, bad
+
+
+def _ocall(lib, **kw):
+    a = dict(h=P, W=P, t=P, B=2, T=4, H=64, V=128, cp=1, beta=0.1, loss=P, seq=P, gh=P, gW=P,
+             ws=P, wsb=1 << 30, dt=BF16, stream=None)
+    a.update(kw)
+    return lib.flce_orpo_fwd_bwd(a["h"], a["W"], a["t"], a["B"], a["T"], a["H"], a["V"],
+                                 a["cp"], ctypes.c_float(a["beta"]), a["loss"], a["seq"],
+                                 a["gh"], a["gW"], a["ws"], a["wsb"], a["dt"], a["stream"])
+
+
+def test_orpo_entry_validates(lib):
+    for field in ["h", "W", "t", "loss", "gh", "gW", "ws"]:
+        assert _ocall(lib, **{field: None}) == INVALID, field
+    for field, value in [("B", 0), ("T", 0), ("H", 0), ("V", -1), ("cp", 0), ("dt", 7),
+                         ("beta", float("nan")), ("beta", float("inf"))]:
+        assert _ocall(lib, **{field: value}) == INVALID, (field, value)
+    for field in ["h", "W", "gh", "gW", "ws"]:
+        assert _ocall(lib, **{field: P + 8}) == UNSUPPORTED, field
+    for field in ["t", "loss", "seq"]:
+        assert _ocall(lib, **{field: P + 2}) == UNSUPPORTED, field
+    assert _ocall(lib, H=72) == UNSUPPORTED
+    assert _ocall(lib, V=100) == UNSUPPORTED
+    assert _ocall(lib, dt=F32) == UNSUPPORTED
+    need = lib.flce_orpo_workspace_bytes(2, 4, 64, 128, 1, BF16)
+    assert need > 0 and _ocall(lib, wsb=need - 1) == WORKSPACE
 
 
 def test_status_strings(lib):
