@@ -52,11 +52,14 @@ def parse_args():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=4096)
-    p.add_argument("--op", choices=("flce", "ce", "vocab", "rmsnorm"), default="flce",
+    p.add_argument("--op", choices=("flce", "ce", "vocab", "rmsnorm", "orpo"), default="flce",
                    help="flce: the fused head (default); ce: cross entropy on given bf16 "
                         "logits [1024, 128256] (flce_cross_entropy); vocab: the fused head "
                         "through flce_fwd_bwd_vocab (vocabulary chunks); rmsnorm: the head "
-                        "behind an RMSNorm (flce_fwd_bwd_rmsnorm)")
+                        "behind an RMSNorm (flce_fwd_bwd_rmsnorm); orpo: the odds-ratio "
+                        "preference loss over the head (flce_orpo_fwd_bwd)")
+    p.add_argument("--pairs", type=int, default=4, help="preference pairs of --op orpo")
+    p.add_argument("--chunk-pairs", type=int, default=2, help="pairs per chunk of --op orpo")
     p.add_argument("--vchunk", type=int, default=16384,
                    help="vocabulary chunk of --op vocab")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -351,13 +354,111 @@ def bench_rmsnorm(args) -> int:
     return 0
 
 
+def bench_orpo(args) -> int:
+    """The odds-ratio preference loss over the head (flce_orpo_fwd_bwd) on a
+    workload's head and hidden-state distribution: its N rows read as
+    2 * pairs sequences (chosen first) of N / (2 pairs) tokens, each
+    sequence's first up-to-256 rows a prompt and last up-to-128 rows padding
+    (targets marked ignored), beta 0.1, chunks of --chunk-pairs pairs.  The
+    three contractions run over every row: 6 N V H flops a call."""
+    import numpy as np
+    import torch
+
+    import linear_cross_entropy_06_amd as flce
+    from synth import config_by_name, make_inputs, mask_preference_rows
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    flce.load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg = config_by_name(args.workload)
+    N, H, V, B, cp, beta = cfg.N, cfg.H, cfg.V, args.pairs, args.chunk_pairs, 0.1
+    if N % (2 * B):
+        print(f"bench.py: {N} rows do not split into {2 * B} sequences", file=sys.stderr)
+        return 1
+    T = N // (2 * B)
+    inp = make_inputs(cfg, seed=args.seed)
+    t_cpu = mask_preference_rows(inp.t, B, T, seed=args.seed, prompt_max=256, pad_max=128)
+    h, W, t = inp.h.to(dev), inp.W.to(dev), t_cpu.to(dev)
+    need = flce.orpo_workspace_bytes(B, T, H, V, cp, h.dtype)
+    if need == 0:
+        print(f"bench.py: {cfg.name} is not a shape flce_orpo_fwd_bwd runs", file=sys.stderr)
+        return 1
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    seq = torch.empty(2 * B, dtype=torch.float32, device=dev)
+    gh = torch.empty_like(h)
+    gw = torch.empty((V, H), dtype=torch.float32, device=dev)
+    kw = dict(loss=loss, seq_logp=seq, grad_h=gh, grad_W=gw, workspace=ws)
+    for _ in range(max(1, args.warmup)):
+        flce.orpo_fwd_bwd(h, W, t, B, T, beta, cp, **kw)
+    torch.cuda.synchronize()
+    loss0 = float(loss)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        flce.orpo_fwd_bwd(h, W, t, B, T, beta, cp, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    flops = 6.0 * N * V * H
+    out = {
+        "metric": "ORPO over the fused head, fwd+bwd tokens/s",
+        "value": N / (ms * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; the workload's h, W and targets, prompt and padding "
+                "rows marked ignored)",
+        "config": {"workload": cfg.name, "N": N, "H": H, "V": V, "pairs": B, "seq_len": T,
+                   "chunk_pairs": cp, "beta": beta, "seed": args.seed},
+        "counted_rows": int((t_cpu >= 0).sum()),
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "workspace_bytes": need,
+        "naive_logits_bytes": N * V * 4,
+        "loss": loss0,
+        "roofline": {
+            "kernel": "orpo_fwd_bwd (all launches of one call)", "bound": "mfma",
+            "achieved": flops / (ev_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": flops / (ev_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "traffic": None, "work_per_launch": f"6*{N}*{V}*{H} = {flops:.4e} flop",
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from synth import to_float64
+        S = 512  # one pair of 512-token sequences
+        rows = np.r_[0:S, T:T + S]  # first S rows of sequence 0 (chosen) and 1
+        hh = to_float64(inp.h[torch.from_numpy(rows)])
+        WW = to_float64(inp.W)
+        tt = t_cpu[torch.from_numpy(rows)].numpy().astype(np.int64)
+        c0 = time.perf_counter()
+        oracle.orpo(hh, WW, tt, 1, S, beta)
+        dt = time.perf_counter() - c0
+        out["cpu_baseline"] = {
+            "value": 2 * S / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"one pair of {S}-token sequences (rows of the workload) against the "
+                      f"full {V}x{H} head, fp64 numpy orpo: {dt:.2f} s"}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
-    if args.op in ("ce", "vocab", "rmsnorm"):
+    if args.op in ("ce", "vocab", "rmsnorm", "orpo"):
         if args.gpus != 1:
             print("bench.py: this build runs on one GPU only", file=sys.stderr)
             return 2
-        return {"ce": bench_ce, "vocab": bench_vocab, "rmsnorm": bench_rmsnorm}[args.op](args)
+        return {"ce": bench_ce, "vocab": bench_vocab, "rmsnorm": bench_rmsnorm,
+                "orpo": bench_orpo}[args.op](args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
