@@ -29,7 +29,10 @@
  *    failed check returns a status and enqueues nothing.
  *  - Requirements: H % 8 == 0 and 16-byte aligned h, W, grad_h, grad_W and
  *    workspace (FLCE_ERR_UNSUPPORTED otherwise); all sizes below 2^31 and
- *    N, H, V, chunk >= 1 (FLCE_ERR_INVALID_ARG otherwise).
+ *    N, H, V, chunk >= 1 (FLCE_ERR_INVALID_ARG otherwise).  A chunk whose
+ *    logits or hidden rows would exceed 2^56 elements is FLCE_ERR_UNSUPPORTED
+ *    (the workspace functions return 0 for it), so every size and offset is
+ *    exact in 64-bit arithmetic.
  *  - Targets must lie in [0, V).  An out-of-range target is not read
  *    through: it makes that token's loss, and so the returned loss, NaN.
  */
@@ -318,8 +321,9 @@ size_t flce_vocab_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t vchun
  * makes the loss NaN (targets are never read on the host).
  * Supported: FLCE_BF16 with H % 64 == 0, V % 8 == 0 and H below 2^22;
  * otherwise FLCE_ERR_UNSUPPORTED.  FLCE_ERR_INVALID_ARG for a null required
- * pointer, pairs, seq_len or chunk_pairs < 1, more than 2^31 - 1 rows, or a
- * beta that is not finite.  Alignment, workspace and stream rules as
+ * pointer, pairs, seq_len or chunk_pairs < 1, more than 2^31 - 1 rows, a
+ * chunk of logits or hidden rows beyond 2^56 elements, or a beta that is not
+ * finite.  Alignment, workspace and stream rules as
  * flce_fwd_bwd (seq_logp 4-byte aligned).
  */
 flce_status flce_orpo_fwd_bwd(const void* h, const void* W, const int32_t* targets,

@@ -30,6 +30,10 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 inline bool dims_ok(int64_t a) { return a >= 1 && a <= kMaxDim; }
 
+// rows x cols elements stay below 2^56, so every workspace size (a few such
+// areas times at most 8 bytes) is exact in int64.  Positive arguments.
+inline bool area_ok(int64_t rows, int64_t cols) { return rows <= (int64_t{1} << 56) / cols; }
+
 inline bool dtype_ok(flce_dtype dt) { return dt == FLCE_BF16 || dt == FLCE_F32; }
 
 inline int64_t esize(flce_dtype dt) { return dt == FLCE_BF16 ? 2 : 4; }
@@ -92,6 +96,7 @@ extern "C" size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t 
                                        flce_dtype dt) {
   if (!dims_ok(N) || !dims_ok(H) || !dims_ok(V) || chunk < 1 || !dtype_ok(dt)) return 0;
   const int64_t C = chunk < N ? chunk : N;
+  if (!area_ok(C, V) || !area_ok(C, H)) return 0;
   // bf16 logits of one chunk + 2 floats per row and half tile (+ grad_h
   // K-split parts for short chunks)
   if (exp_path(H, V, dt)) return static_cast<size_t>(exp_layout(N, C, H, V).total);
@@ -152,6 +157,7 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
     return FLCE_ERR_UNSUPPORTED;
   if (events && n_events < 2 * flce_launch_count(N, chunk)) return FLCE_ERR_INVALID_ARG;
   const size_t need = flce_workspace_bytes(N, H, V, chunk, dt);
+  if (need == 0) return FLCE_ERR_UNSUPPORTED;  // a chunk of logits beyond 2^56 elements
   if (workspace_bytes < need) return FLCE_ERR_WORKSPACE;
 
   Marks mk{events, stream};
@@ -425,6 +431,7 @@ extern "C" flce_status flce_fwd_bwd_rmsnorm(const void* x, const void* gamma, fl
       !aligned16(workspace) || (reinterpret_cast<uintptr_t>(grad_gamma) & 3u))
     return FLCE_ERR_UNSUPPORTED;
   const size_t need = flce_rmsnorm_workspace_bytes(N, H, V, chunk, dt);
+  if (need == 0) return FLCE_ERR_UNSUPPORTED;
   if (workspace_bytes < need) return FLCE_ERR_WORKSPACE;
   const int64_t C = chunk < N ? chunk : N;
   const NormLayout lay = norm_layout(flce_workspace_bytes(N, H, V, chunk, dt), C, H, esize(dt));
@@ -487,6 +494,7 @@ extern "C" size_t flce_vocab_workspace_bytes(int64_t N, int64_t H, int64_t V, in
   if (!dims_ok(N) || !dims_ok(H) || !dims_ok(V) || vchunk < 1 || !dtype_ok(dt)) return 0;
   if (!vocab_path_ok(H, V, vchunk, dt)) return 0;
   const int64_t Vc = vchunk < V ? vchunk : V;
+  if (!area_ok(N, Vc) || !area_ok(N, H) || !area_ok(N, V)) return 0;
   return static_cast<size_t>(vocab_layout(N, H, V, Vc).total);
 }
 
@@ -504,8 +512,9 @@ extern "C" flce_status flce_fwd_bwd_vocab(const void* h, const void* W, const in
       (reinterpret_cast<uintptr_t>(loss) & 3u))
     return FLCE_ERR_UNSUPPORTED;
   if (!vocab_path_ok(H, V, vchunk, dt)) return FLCE_ERR_UNSUPPORTED;
-  if (workspace_bytes < flce_vocab_workspace_bytes(N, H, V, vchunk, dt))
-    return FLCE_ERR_WORKSPACE;
+  const size_t need = flce_vocab_workspace_bytes(N, H, V, vchunk, dt);
+  if (need == 0) return FLCE_ERR_UNSUPPORTED;
+  if (workspace_bytes < need) return FLCE_ERR_WORKSPACE;
 
   const int64_t Vc = vchunk < V ? vchunk : V;
   const VocabLayout lay = vocab_layout(N, H, V, Vc);
@@ -625,7 +634,8 @@ inline bool orpo_args_ok(int64_t B, int64_t T, int64_t H, int64_t V, int64_t Pc,
                          flce_dtype dt) {
   if (B < 1 || T < 1 || Pc < 1 || !dims_ok(H) || !dims_ok(V) || !dtype_ok(dt)) return false;
   if (B > kMaxDim / 2 || T > kMaxDim / (2 * B)) return false;  // 2 B T rows fit an int
-  return true;
+  const int64_t R = 2 * (Pc < B ? Pc : B) * T;                 // rows of a chunk
+  return area_ok(R, V) && area_ok(R, H);
 }
 
 }  // namespace

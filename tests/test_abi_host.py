@@ -324,6 +324,24 @@ def test_orpo_entry_validates(lib):
     assert need > 0 and _ocall(lib, wsb=need - 1) == WORKSPACE
 
 
+def test_workspace_sizes_that_would_overflow_are_refused(lib):
+    """A chunk of logits beyond 2^56 elements: the workspace functions return
+    0 and the entry points refuse before computing an offset."""
+    big = 2 ** 31 - 1
+    assert lib.flce_workspace_bytes(big, 64, big, big, BF16) == 0
+    assert lib.flce_workspace_bytes(big, 64, big, big, F32) == 0
+    assert lib.flce_rmsnorm_workspace_bytes(big, 64, big, big, BF16) == 0
+    assert lib.flce_orpo_workspace_bytes(2 ** 28, 2, 64, big - 7, 2 ** 28, BF16) == 0
+    # the largest sizes below the bound still get an exact size
+    assert lib.flce_workspace_bytes(2 ** 20, 64, 2 ** 30, 2 ** 20, F32) == 2 ** 52
+    st = lib.flce_fwd_bwd(P, P, P, big, 64, big, big, P, P, P, P, 1 << 62, BF16, None)
+    assert st == UNSUPPORTED
+    st = _rcall(lib, N=big, H=64, V=big, chunk=big, wsb=1 << 62)
+    assert st == UNSUPPORTED
+    assert _ocall(lib, B=2 ** 28, T=2, V=big - 7, cp=2 ** 28, wsb=1 << 62) == INVALID
+    # (the vocabulary-chunked path needs H, V < 2^22, so its areas stay below 2^53)
+
+
 def test_status_strings(lib):
     for code in range(5):
         s = lib.flce_status_string(code).decode()
