@@ -20,7 +20,7 @@ from .flce_oracle import (
     rmsnorm,
     row_losses,
 )
-from .orpo_oracle import orpo, token_logp
+from .orpo_oracle import orpo, orpo_sampled, token_logp
 
 __all__ = [
     "dlogits",
@@ -33,6 +33,7 @@ __all__ = [
     "logits",
     "logsumexp_rows",
     "orpo",
+    "orpo_sampled",
     "rmsnorm",
     "row_losses",
     "token_logp",

@@ -72,15 +72,12 @@ def token_logp(h: np.ndarray, W: np.ndarray, t: np.ndarray):
     return logp, P, counted
 
 
-def orpo(h, W, t, pairs: int, seq_len: int, beta: float):
-    """ORPO loss and gradients; returns (loss, grad_h, grad_W, seq_logp)
-    with seq_logp[s] the mean log-probability l_s of sequence s."""
-    h = np.asarray(h, dtype=np.float64)
-    W = np.asarray(W, dtype=np.float64)
-    t = np.asarray(t)
+def objective(logp: np.ndarray, counted: np.ndarray, pairs: int, seq_len: int,
+              beta: float):
+    """The objective from per-row log-probabilities: returns (loss, c, l_seq)
+    with c_r = -dloss/dlog p_r (0 for rows that do not count) and l_seq the
+    mean log-probability of every sequence."""
     B, T = pairs, seq_len
-    _split(t, B, T)
-    logp, P, counted = token_logp(h, W, t)
     lp = logp.reshape(2 * B, T)
     cnt = counted.reshape(2 * B, T).sum(axis=1).astype(np.float64)
     with np.errstate(divide="ignore", invalid="ignore"):
@@ -102,9 +99,65 @@ def orpo(h, W, t, pairs: int, seq_len: int, beta: float):
     c = np.repeat(per_seq, T)
     c[: B * T] += 1.0 / M if M > 0 else math.nan
     c = np.where(counted, c, 0.0)
-    G = P.copy()
+    return loss, c, l_seq
+
+
+def orpo(h, W, t, pairs: int, seq_len: int, beta: float):
+    """ORPO loss and gradients; returns (loss, grad_h, grad_W, seq_logp)
+    with seq_logp[s] the mean log-probability l_s of sequence s."""
+    h = np.asarray(h, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    t = np.asarray(t)
+    _split(t, pairs, seq_len)
+    logp, P, counted = token_logp(h, W, t)
+    loss, c, l_seq = objective(logp, counted, pairs, seq_len, beta)
+    G = P
     rows = np.nonzero(counted)[0]
     G[rows, t[rows]] -= 1.0
     G *= c[:, None]
     return loss, G @ W, G.T @ h, l_seq
 
+
+def orpo_sampled(h, W, t, pairs: int, seq_len: int, beta: float, rows=(), vocab_rows=(),
+                 chunk: int = 1024):
+    """The same objective at any size: streams the logits over row chunks
+    (a [chunk, V] block at a time) for every row's log-sum-exp and target
+    log-probability, then forms only the requested rows of grad_h and of
+    grad_W.  Returns a dict with ``loss``, ``seq_logp`` [2 pairs], ``lse``
+    [N], ``grad_h_rows`` [len(rows), H] and ``grad_W_rows``
+    [len(vocab_rows), H]."""
+    h = np.asarray(h, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    t = np.asarray(t, dtype=np.int64)
+    _split(t, pairs, seq_len)
+    if np.any(t >= W.shape[0]):
+        raise ValueError("target >= V")
+    N = h.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    vocab_rows = np.asarray(vocab_rows, dtype=np.int64)
+    counted = t >= 0
+    lse = np.empty(N)
+    logp = np.zeros(N)
+    for r0 in range(0, N, chunk):
+        r1 = min(N, r0 + chunk)
+        Z = h[r0:r1] @ W.T
+        m = Z.max(axis=1, keepdims=True)
+        lse[r0:r1] = (m + np.log(np.exp(Z - m).sum(axis=1, keepdims=True)))[:, 0]
+        k = np.nonzero(counted[r0:r1])[0]
+        logp[r0 + k] = Z[k, t[r0 + k]] - lse[r0 + k]
+        del Z
+    loss, c, l_seq = objective(logp, counted, pairs, seq_len, beta)
+    gh = np.zeros((rows.size, h.shape[1]))
+    if rows.size:
+        Zr = h[rows] @ W.T
+        Gr = np.exp(Zr - lse[rows, None])
+        k = np.nonzero(counted[rows])[0]
+        Gr[k, t[rows[k]]] -= 1.0
+        gh = (Gr * c[rows, None]) @ W
+    gw = np.zeros((vocab_rows.size, h.shape[1]))
+    if vocab_rows.size:
+        GJ = np.exp(h @ W[vocab_rows].T - lse[:, None])
+        GJ -= (t[:, None] == vocab_rows[None, :])
+        gw = (GJ * c[:, None]).T @ h
+    return {"loss": loss, "seq_logp": l_seq, "lse": lse, "grad_h_rows": gh,
+            "grad_W_rows": gw}

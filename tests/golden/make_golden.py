@@ -1,6 +1,7 @@
 """Write the oracle's expected values for the full-size workloads.
 
     python tests/golden/make_golden.py [config ...]      (default: 2 3 4 5)
+    python tests/golden/make_golden.py orpo              (preference batch)
 
 Calls only ``synth`` (seeded inputs) and ``oracle`` (fp64 reference).  For
 each workload it stores, in ``cfg<k>_sampled.npz``: the mean loss, the
@@ -22,7 +23,12 @@ ROOT = os.path.dirname(os.path.dirname(HERE))
 sys.path.insert(0, ROOT)
 
 import oracle  # noqa: E402
-from synth import CONFIGS, make_inputs, to_float64  # noqa: E402
+from synth import CONFIGS, make_inputs, mask_preference_rows, to_float64  # noqa: E402
+
+# The preference batch the benchmark times: workload 3's rows as 4 pairs of
+# 1024-token sequences, prompts of up to 256 and padding of up to 128 rows
+# ignored, beta 0.1.
+ORPO = dict(config=3, pairs=4, seq_len=1024, prompt_max=256, pad_max=128, beta=0.1)
 
 
 def sample_rows(cfg, t: np.ndarray):
@@ -64,7 +70,52 @@ def make(idx: int) -> str:
     return out
 
 
+def make_orpo() -> str:
+    cfg = CONFIGS[ORPO["config"]]
+    B, T = ORPO["pairs"], ORPO["seq_len"]
+    t0 = time.perf_counter()
+    x = make_inputs(cfg, seed=0)
+    tm = mask_preference_rows(x.t, B, T, seed=0, prompt_max=ORPO["prompt_max"],
+                              pad_max=ORPO["pad_max"])
+    h, W, t = to_float64(x.h), to_float64(x.W), tm.numpy().astype(np.int64)
+    N, V = cfg.N, cfg.V
+    rng = np.random.default_rng([0, 98])
+    # sequence starts and ends, the chunk boundary of 2-pair chunks, a prompt
+    # row (ignored), the last counted row of a sequence, a few random rows
+    rows = {0, T - 1, T, 2 * T - 1, B * T - 1, B * T, N - 1, 2 * T, 2 * T * B // 2}
+    rows |= {int(np.nonzero(t < 0)[0][0]), int(np.nonzero(t[:T] >= 0)[0][-1])}
+    rows |= set(rng.integers(0, N, 5).tolist())
+    rows = np.array(sorted(rows))
+    vals, counts = np.unique(t[t >= 0], return_counts=True)
+    vocab = {0, 1, V // 2, V - 1, int(vals[np.argmax(counts)])}
+    vocab |= {int(t[r]) for r in rows if t[r] >= 0}
+    vocab |= set(rng.integers(0, V, 4).tolist())
+    vocab = np.array(sorted(vocab))
+    r = oracle.orpo_sampled(h, W, t, B, T, ORPO["beta"], rows=rows, vocab_rows=vocab,
+                            chunk=1024)
+    out = os.path.join(HERE, "orpo_llama3_8b_head_sampled.npz")
+    np.savez_compressed(
+        out,
+        config=np.array(cfg.name),
+        seed=np.array(0),
+        pairs=np.array(B),
+        seq_len=np.array(T),
+        prompt_max=np.array(ORPO["prompt_max"]),
+        pad_max=np.array(ORPO["pad_max"]),
+        beta=np.array(ORPO["beta"]),
+        loss=np.array(r["loss"]),
+        seq_logp=r["seq_logp"],
+        rows=rows,
+        vocab_rows=vocab,
+        grad_h_rows=r["grad_h_rows"].astype(np.float32),
+        grad_W_rows=r["grad_W_rows"].astype(np.float32),
+    )
+    print(f"orpo {cfg.name}: loss={r['loss']:.9f} rows={len(rows)} vocab_rows={len(vocab)} "
+          f"({time.perf_counter() - t0:.1f} s) -> {out}", flush=True)
+    return out
+
+
 if __name__ == "__main__":
-    ids = [int(a) for a in sys.argv[1:]] or [2, 3, 4, 5]
-    for i in ids:
-        make(i)
+    args = sys.argv[1:] or ["2", "3", "4", "5"]
+    for a in args:
+        make_orpo() if a == "orpo" else make(int(a))

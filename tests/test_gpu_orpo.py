@@ -184,3 +184,44 @@ def test_orpo_llama2_like_head(flce):
     got = flce.orpo_fwd_bwd(h.cuda(), W.cuda(), t.cuda(), B, T, 0.1, 1)
     torch.cuda.synchronize()
     _check("orpo llama2-like", got, _oracle(h, W, t, B, T, 0.1))
+
+
+def test_orpo_full_size_sampled(flce):
+    """The benchmark's preference batch (Llama-3-8B head, 4 pairs of 1024
+    tokens, prompts and padding ignored, beta 0.1) in the benchmark's launch
+    configuration (2 pairs a chunk): loss, every sequence's mean
+    log-probability and sampled rows of grad_h and grad_W against the
+    oracle's stored values, plus properties that hold at any size (columns
+    of grad_W sum to zero; ignored rows have zero grad_h)."""
+    import os
+    from synth import CONFIGS, make_inputs
+    p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                     "orpo_llama3_8b_head_sampled.npz")
+    if not os.path.exists(p):
+        pytest.fail(f"missing {p}: run tests/golden/make_golden.py orpo")
+    gold = np.load(p, allow_pickle=False)
+    B, T, beta = int(gold["pairs"]), int(gold["seq_len"]), float(gold["beta"])
+    say("orpo full size: generating inputs")
+    inp = make_inputs(CONFIGS[3], seed=0)
+    t = mask_preference_rows(inp.t, B, T, seed=0, prompt_max=int(gold["prompt_max"]),
+                             pad_max=int(gold["pad_max"]))
+    h, W, td = inp.h.cuda(), inp.W.cuda(), t.cuda()
+    del inp
+    say(f"orpo full size: pairs={B} seq_len={T} chunk_pairs=2")
+    loss, seq, gh, gw = flce.orpo_fwd_bwd(h, W, td, B, T, beta, 2)
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(gold["rows"]).cuda()
+    vrows = torch.from_numpy(gold["vocab_rows"]).cuda()
+    el = rel(float(loss), float(gold["loss"]))
+    es = float(np.max(np.abs(f64(seq) - gold["seq_logp"]) / np.abs(gold["seq_logp"])))
+    eh = rel_fro(f64(gh[rows]), gold["grad_h_rows"])
+    ew = rel_fro(f64(gw[vrows]), gold["grad_W_rows"])
+    colsum = gw.double().sum(dim=0).abs().max().item()
+    scale = gw.double().abs().sum(dim=0).max().item()
+    ignored = torch.count_nonzero(gh[td < 0]).item()
+    say(f"  loss {float(loss):.7f} vs {float(gold['loss']):.7f} rel {el:.2e}; seq_logp "
+        f"{es:.2e}; grad_h rows {eh:.2e}; grad_W rows {ew:.2e}; |sum_j grad_W| {colsum:.2e} "
+        f"(sum |.| {scale:.2e}); nonzero ignored grad_h {ignored}")
+    assert el <= LOSS_RTOL and es <= 1e-4 and eh <= GRAD_RTOL and ew <= GRAD_RTOL
+    assert colsum <= 1e-3 * scale
+    assert ignored == 0

@@ -24,7 +24,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import flce, orpo
+from oracle import flce, orpo, orpo_sampled
 
 
 def _rand(B, T, H, V, seed=0, h_std=1.0, w_std=0.5, ignore=()):
@@ -167,6 +167,22 @@ def test_orpo_empty_sequence_is_nan():
     t[3:] = -100  # the rejected sequence has no counted row
     loss, gh, gw, seq = orpo(h, W, t, 1, 3, 0.1)
     assert math.isnan(loss) and math.isnan(seq[1])
+
+
+@pytest.mark.parametrize("chunk", [1, 5, 7, 1000])
+def test_orpo_sampled_equals_orpo(chunk):
+    """The streamed form (for full-size expected values) against the pinned
+    definition, for chunk sizes that do and do not divide the rows."""
+    B, T, H, V, beta = 3, 5, 6, 11, 0.6
+    h, W, t = _rand(B, T, H, V, seed=8, ignore=(0, 6, 7, 20, 29))
+    loss, gh, gw, seq = orpo(h, W, t, B, T, beta)
+    rows = np.array([0, 3, 6, 14, 29])
+    vocab = np.array([0, 4, 10])
+    r = orpo_sampled(h, W, t, B, T, beta, rows=rows, vocab_rows=vocab, chunk=chunk)
+    assert abs(r["loss"] - loss) <= 1e-12 * abs(loss)
+    _close(r["seq_logp"], seq)
+    _close(r["grad_h_rows"], gh[rows])
+    _close(r["grad_W_rows"], gw[vocab])
 
 
 # planted mistakes ----------------------------------------------------------
