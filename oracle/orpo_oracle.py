@@ -19,7 +19,8 @@ without Reference Model", 2024), written out from its definition:
     counted     a row counts when its target is >= 0 (a negative target
                 marks a prompt or padding position)
     log p_r     = Z[r, t_r] - lse_r,  Z = h W^T             (per counted row)
-    l_s         = mean of log p_r over the counted rows of sequence s
+    l_s         = min(mean of log p_r over the counted rows of sequence s,
+                      -2^-20)
     logodds_s   = l_s - ln(1 - exp(l_s))
     L_OR        = -(1/B) sum_b ln sigmoid(logodds_b - logodds_{B+b})
     L_SFT       = -(1/M) sum of log p_r over the counted chosen rows
@@ -34,8 +35,18 @@ of pair b,
     c_r = 1/M [chosen only] + beta/B * sigmoid(-(lo_b - lo_{B+b}))
           * (+1 chosen, -1 rejected) / ((1 - exp(l_s)) n_s)
 
-with n_s the counted rows of the row's sequence s.  A sequence with no
-counted row has no mean log-probability; the result is then NaN.
+with n_s the counted rows of the row's sequence s, and no odds-ratio part
+for a sequence whose mean sits at the floor.  A sequence with no counted
+row has no mean log-probability; the result is then NaN.
+
+The floor -2^-20 on l_s is a reading of this build, not the paper's: as a
+sequence becomes certain (every token's probability near 1) l_s -> 0 and
+ln(1 - exp(l_s)) -> -inf, and in fp32 the per-token log-probabilities
+(differences of log-sum-exp and target logit, magnitudes ~10-20) carry
+absolute errors near 2^-20, so a mean above the floor is not resolvable and
+may even round to >= 0.  At the floor the odds-ratio term is constant in
+that sequence's log-probabilities (the derivative of the min), so such a
+sequence still gets its SFT gradient and a finite loss.
 """
 
 from __future__ import annotations
@@ -43,6 +54,9 @@ from __future__ import annotations
 import math
 
 import numpy as np
+
+# Upper bound of a sequence's mean log-probability (see the module notes).
+LOGP_FLOOR = -(2.0 ** -20)
 
 
 def _split(t: np.ndarray, pairs: int, seq_len: int):
@@ -81,7 +95,9 @@ def objective(logp: np.ndarray, counted: np.ndarray, pairs: int, seq_len: int,
     lp = logp.reshape(2 * B, T)
     cnt = counted.reshape(2 * B, T).sum(axis=1).astype(np.float64)
     with np.errstate(divide="ignore", invalid="ignore"):
-        l_seq = lp.sum(axis=1) / cnt                     # mean log p per sequence
+        l_raw = lp.sum(axis=1) / cnt                     # mean log p per sequence
+        at_floor = l_raw > LOGP_FLOOR                    # False for NaN
+        l_seq = np.where(at_floor, LOGP_FLOOR, l_raw)
         logodds = l_seq - np.log1p(-np.exp(l_seq))       # ln(P / (1 - P))
     ratio = logodds[:B] - logodds[B:]
     # -ln sigmoid(x) = ln(1 + exp(-x)), written stably
@@ -96,6 +112,7 @@ def objective(logp: np.ndarray, counted: np.ndarray, pairs: int, seq_len: int,
     with np.errstate(divide="ignore", invalid="ignore"):
         per_seq = beta / B * np.concatenate([sig_neg, -sig_neg]) / (
             (1.0 - np.exp(l_seq)) * cnt)
+    per_seq = np.where(at_floor, 0.0, per_seq)
     c = np.repeat(per_seq, T)
     c[: B * T] += 1.0 / M if M > 0 else math.nan
     c = np.where(counted, c, 0.0)

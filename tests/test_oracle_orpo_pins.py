@@ -13,7 +13,10 @@ Facts that do not come from the oracle's own code:
 * rows whose target is negative do not count: changing their hidden state
   changes nothing and their grad_h rows are zero;
 * swapping the chosen and rejected halves changes the odds-ratio term by
-  the mean log odds ratio (ln sigmoid(x) - ln sigmoid(-x) = x).
+  the mean log odds ratio (ln sigmoid(x) - ln sigmoid(-x) = x);
+* a sequence the model is certain of (every token's probability 1 - 1e-17)
+  sits at the floor of the mean log-probability: the loss and gradients stay
+  finite and equal torch's (its formulation clamps the mean the same way).
 ``test_orpo_mutants_are_caught`` plants plausible mistakes in copies and
 checks that a pin rejects each.
 """
@@ -44,10 +47,11 @@ def _close(a, b, rtol=1e-10, atol=1e-13):
     assert np.allclose(a, b, rtol=rtol, atol=atol), float(np.max(np.abs(a - b)))
 
 
-def pin_torch(impl):
-    B, T, H, V, beta = 3, 4, 6, 9, 0.7
-    h, W, t = _rand(B, T, H, V, seed=1, ignore=(0, 1, 13, 22))
-    loss, gh, gw, seq = impl(h, W, t, B, T, beta)
+FLOOR = -(2.0 ** -20)
+
+
+def _torch_ref(h, W, t, B, T, beta):
+    """torch fp64: the objective in torch's own ops, gradients by autograd."""
     ht = torch.tensor(h, requires_grad=True)
     Wt = torch.tensor(W, requires_grad=True)
     tt = torch.tensor(t)
@@ -56,15 +60,24 @@ def pin_torch(impl):
     mask = tt >= 0
     tok = lsm.gather(1, tt.clamp(min=0)[:, None])[:, 0] * mask
     mean_lp = tok.view(2 * B, T).sum(dim=1) / mask.view(2 * B, T).sum(dim=1)
+    mean_lp = torch.clamp(mean_lp, max=FLOOR)
     lo = mean_lp - torch.log(-torch.expm1(mean_lp))
     l_or = -torch.nn.functional.logsigmoid(lo[:B] - lo[B:]).mean()
     l_sft = torch.nn.functional.cross_entropy(z[: B * T], tt[: B * T], ignore_index=-100)
     lt = l_sft + beta * l_or
     lt.backward()
-    assert abs(loss - lt.item()) <= 1e-12 * max(1.0, abs(lt.item()))
-    _close(seq, mean_lp.detach().numpy())
-    _close(gh, ht.grad.numpy())
-    _close(gw, Wt.grad.numpy())
+    return lt.item(), ht.grad.numpy(), Wt.grad.numpy(), mean_lp.detach().numpy()
+
+
+def pin_torch(impl):
+    B, T, H, V, beta = 3, 4, 6, 9, 0.7
+    h, W, t = _rand(B, T, H, V, seed=1, ignore=(0, 1, 13, 22))
+    loss, gh, gw, seq = impl(h, W, t, B, T, beta)
+    lt, gh_t, gw_t, seq_t = _torch_ref(h, W, t, B, T, beta)
+    assert abs(loss - lt) <= 1e-12 * max(1.0, abs(lt))
+    _close(seq, seq_t)
+    _close(gh, gh_t)
+    _close(gw, gw_t)
 
 
 def pin_finite_differences(impl):
@@ -153,8 +166,27 @@ def pin_swap_halves(impl):
     assert abs(lhs - beta * mean_ratio) <= 1e-11, (lhs, mean_ratio)
 
 
+def pin_certain_sequence(impl):
+    """Chosen sequence 0 certain: W = 5 I, its rows h = 8 e_t, so each of its
+    tokens has logit margin 40 and log p ~ -1e-17 (mean above the floor)."""
+    B, T, V, beta = 2, 3, 5, 0.8
+    h, _, t = _rand(B, T, V, V, seed=10, ignore=(8,))
+    W = 5.0 * np.eye(V)
+    for r in range(T):
+        h[r] = 0.0
+        h[r, t[r]] = 8.0
+    loss, gh, gw, seq = impl(h, W, t, B, T, beta)
+    assert np.isfinite(loss) and np.all(np.isfinite(gh)) and np.all(np.isfinite(gw))
+    assert seq[0] == FLOOR
+    lt, gh_t, gw_t, seq_t = _torch_ref(h, W, t, B, T, beta)
+    assert abs(loss - lt) <= 1e-12 * max(1.0, abs(lt))
+    _close(seq, seq_t)
+    _close(gh, gh_t)
+    _close(gw, gw_t)
+
+
 PINS = [pin_torch, pin_finite_differences, pin_w_zero, pin_beta_zero_is_head_on_chosen,
-        pin_ignored_rows, pin_swap_halves]
+        pin_ignored_rows, pin_swap_halves, pin_certain_sequence]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -204,6 +236,8 @@ def _variant(mistake):
         cnt = counted.reshape(2 * B, T).sum(axis=1).astype(np.float64)
         norm = cnt if mistake != "sum_not_mean" else np.ones(2 * B)
         l_seq = logp.reshape(2 * B, T).sum(axis=1) / norm
+        floor = l_seq > FLOOR if mistake != "no_floor" else np.zeros(2 * B, bool)
+        l_seq = np.where(floor, FLOOR, l_seq)
         lo = l_seq - np.log1p(-np.exp(l_seq)) if mistake != "odds_is_prob" else l_seq
         ratio = lo[:B] - lo[B:]
         red = np.mean if mistake != "or_sum" else np.sum
@@ -216,6 +250,7 @@ def _variant(mistake):
         dlo = 1.0 / (1.0 - np.exp(l_seq)) if mistake != "odds_is_prob" else np.ones(2 * B)
         scale = 1.0 / B if mistake != "or_sum" else 1.0
         per_seq = beta * scale * np.concatenate([sig, rej]) * dlo / norm
+        per_seq = np.where(floor, 0.0, per_seq)
         c = np.repeat(per_seq, T)
         c[sft_rows] += 1.0 / M
         c = np.where(counted, c, 0.0)
@@ -224,12 +259,16 @@ def _variant(mistake):
         G *= c[:, None]
         return loss, G @ W, G.T @ h, l_seq
 
-    impl.__name__ = f"mut_{mistake}"
-    return impl
+    def quiet(*a):
+        with np.errstate(all="ignore"):  # a planted mistake may divide by zero
+            return impl(*a)
+
+    quiet.__name__ = f"mut_{mistake}"
+    return quiet
 
 
 MUTANTS = ["sum_not_mean", "odds_is_prob", "or_sum", "sft_both", "rejected_sign",
-           "count_ignored"]
+           "count_ignored", "no_floor"]
 
 
 def test_variant_without_mistake_passes_every_pin():
