@@ -6,7 +6,8 @@
 // post-training losses that take the LM-head weight, the hidden states and
 // the targets and return the loss; the objective is the published one of
 // ORPO (Hong, Lee and Thorne, 2024):
-//   l_s      mean over the counted rows of sequence s of log p(t_r)
+//   l_s      min(mean over the counted rows of sequence s of log p(t_r),
+//            -2^-14)
 //   lo_s     = l_s - ln(1 - exp(l_s))                       (log odds)
 //   L_OR     = (1/B) sum_b ln(1 + exp(-(lo_b - lo_{B+b})))
 //   L_SFT    = -(1/M) sum over counted chosen rows of log p(t_r)
@@ -15,7 +16,13 @@
 //   c_r = [chosen] / M + (+/-) beta / B * sigmoid(-(lo_b - lo_{B+b}))
 //         / ((1 - exp(l_s)) n_s)
 // (+ for the chosen, - for the rejected row of pair b; n_s counted rows of
-// the row's sequence).  Sums run in fp64 in a fixed order (deterministic).
+// the row's sequence; no odds-ratio part for a sequence at the floor).  The
+// floor keeps ln(1 - exp(l)) finite when a sequence is certain: an fp32
+// log-probability (log-sum-exp minus target logit) is off by about one unit
+// in the last place of the logits, 2^-18 to 2^-16 at magnitudes 30 to 100,
+// so a mean closer to 0 is not resolvable (and may round to >= 0); at the
+// floor the odds-ratio term does not depend on that sequence.  Sums run in fp64 in a fixed order
+// (deterministic).
 #include "flce_internal.h"
 
 #include <math.h>
@@ -24,6 +31,7 @@ namespace flce {
 namespace {
 
 constexpr double kLn2d = 0.6931471805599453;
+constexpr double kLogpFloor = -6.103515625e-05;  // -2^-14
 constexpr int kWaves = 4;
 constexpr int kCountThreads = 1024;
 constexpr int kLossThreads = 256;
@@ -81,15 +89,19 @@ orpo_coef_kernel(const float* __restrict__ lse2, const float* __restrict__ zt2,
   sl = wave_sum(sl) * kLn2d;
   nw = wave_sum(nw);
   nl = wave_sum(nl);
-  // Mean log-probabilities (0 / 0 = NaN for a sequence with no counted row).
-  const double lw = sw / (double)nw, ll = sl / (double)nl;
+  // Mean log-probabilities (0 / 0 = NaN for a sequence with no counted row;
+  // NaN compares false and stays NaN).
+  double lw = sw / (double)nw, ll = sl / (double)nl;
+  const bool fw = lw > kLogpFloor, fl = ll > kLogpFloor;
+  if (fw) lw = kLogpFloor;
+  if (fl) ll = kLogpFloor;
   const double qw = -expm1(lw), ql = -expm1(ll);  // 1 - P, accurate near P = 1
   const double ratio = (lw - log(qw)) - (ll - log(ql));
   const double or_term = ratio > 0.0 ? log1p(exp(-ratio)) : -ratio + log1p(exp(ratio));
   const double sig_neg = 1.0 / (1.0 + exp(ratio));
   const double k_or = (double)beta / (double)B * sig_neg;
-  const float cw = (float)(1.0 / (double)count[0] + k_or / (qw * (double)nw));
-  const float cl = (float)(-k_or / (ql * (double)nl));
+  const float cw = (float)(1.0 / (double)count[0] + (fw ? 0.0 : k_or / (qw * (double)nw)));
+  const float cl = fl ? 0.0f : (float)(-k_or / (ql * (double)nl));
   for (int k = lane; k < T; k += 64) {
     coef[rw + k] = targets[rw + k] >= 0 ? cw : 0.0f;
     coef[rl + k] = targets[rl + k] >= 0 ? cl : 0.0f;

@@ -20,7 +20,7 @@ without Reference Model", 2024), written out from its definition:
                 marks a prompt or padding position)
     log p_r     = Z[r, t_r] - lse_r,  Z = h W^T             (per counted row)
     l_s         = min(mean of log p_r over the counted rows of sequence s,
-                      -2^-20)
+                      -2^-14)
     logodds_s   = l_s - ln(1 - exp(l_s))
     L_OR        = -(1/B) sum_b ln sigmoid(logodds_b - logodds_{B+b})
     L_SFT       = -(1/M) sum of log p_r over the counted chosen rows
@@ -39,12 +39,13 @@ with n_s the counted rows of the row's sequence s, and no odds-ratio part
 for a sequence whose mean sits at the floor.  A sequence with no counted
 row has no mean log-probability; the result is then NaN.
 
-The floor -2^-20 on l_s is a reading of this build, not the paper's: as a
+The floor -2^-14 on l_s is a reading of this build, not the paper's: as a
 sequence becomes certain (every token's probability near 1) l_s -> 0 and
-ln(1 - exp(l_s)) -> -inf, and in fp32 the per-token log-probabilities
-(differences of log-sum-exp and target logit, magnitudes ~10-20) carry
-absolute errors near 2^-20, so a mean above the floor is not resolvable and
-may even round to >= 0.  At the floor the odds-ratio term is constant in
+ln(1 - exp(l_s)) -> -inf, and in fp32 a per-token log-probability (the
+difference of a log-sum-exp and a target logit) carries an absolute error of
+about one unit in the last place of the logits, 2^-18 to 2^-16 for logits of
+magnitude 30 to 100, so a mean above the floor is not resolvable and may
+even round to >= 0.  At the floor the odds-ratio term is constant in
 that sequence's log-probabilities (the derivative of the min), so such a
 sequence still gets its SFT gradient and a finite loss.
 """
@@ -56,7 +57,7 @@ import math
 import numpy as np
 
 # Upper bound of a sequence's mean log-probability (see the module notes).
-LOGP_FLOOR = -(2.0 ** -20)
+LOGP_FLOOR = -(2.0 ** -14)
 
 
 def _split(t: np.ndarray, pairs: int, seq_len: int):

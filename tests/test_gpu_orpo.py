@@ -87,6 +87,27 @@ def test_orpo_confident_model(flce):
     _check("orpo confident", got, exp, seq_rtol=2e-3)
 
 
+def test_orpo_certain_sequence_stays_finite(flce):
+    """A chosen sequence the model is certain of (W = 5 I, its rows h = 8 e_t:
+    logit margin 40, 1 - p ~ 1e-15) sits at the floor of the mean
+    log-probability on both sides: finite loss and gradients, equal to the
+    oracle's."""
+    B, T, H, V, beta = 2, 8, 256, 256, 0.5
+    h, _, t = _inputs(B, T, H, V, seed=58, prompt_max=2, pad_max=1)
+    W = (5.0 * torch.eye(V, H)).to(torch.bfloat16)
+    for r in range(T):
+        if t[r] >= 0:
+            h[r] = 0.0
+            h[r, int(t[r])] = 8.0
+    say("orpo certain sequence")
+    got = flce.orpo_fwd_bwd(h.cuda(), W.cuda(), t.cuda(), B, T, beta, 1)
+    torch.cuda.synchronize()
+    exp = _oracle(h, W, t, B, T, beta)
+    assert float(got[1][0]) == -(2.0 ** -14) and exp[3][0] == -(2.0 ** -14)
+    assert torch.isfinite(got[2]).all() and torch.isfinite(got[3]).all()
+    _check("orpo certain", got, exp)
+
+
 def test_orpo_w_zero_closed_form(flce):
     B, T, H, V, beta = 3, 20, 64, 512, 0.7
     h, W, t = _inputs(B, T, H, V, seed=52, prompt_max=5, pad_max=5)

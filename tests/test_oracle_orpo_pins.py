@@ -47,7 +47,7 @@ def _close(a, b, rtol=1e-10, atol=1e-13):
     assert np.allclose(a, b, rtol=rtol, atol=atol), float(np.max(np.abs(a - b)))
 
 
-FLOOR = -(2.0 ** -20)
+FLOOR = -(2.0 ** -14)
 
 
 def _torch_ref(h, W, t, B, T, beta):
