@@ -308,7 +308,10 @@ size_t flce_vocab_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t vchun
  *              = (b, pairs + b)
  *   counted    a row counts when its target is >= 0; a negative target
  *              marks a prompt or padding row (no loss, zero gradient row)
- *   l_s        mean of log softmax(h_r W^T)[t_r] over the counted rows of s
+ *   l_s        mean of log softmax(h_r W^T)[t_r] over the counted rows of s,
+ *              at most -2^-14 (a floor: ln(1 - exp(l)) diverges as l -> 0 and
+ *              fp32 log-probabilities cannot resolve l above it; at the floor
+ *              the sequence gets no odds-ratio gradient)
  *   loss       -(1/M) sum over counted chosen rows of log p
  *              + beta * (1/pairs) sum_b ln(1 + exp(-(lo_b - lo_{pairs+b})))
  *              with lo_s = l_s - ln(1 - exp(l_s)) and M the counted chosen
