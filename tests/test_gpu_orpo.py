@@ -196,6 +196,17 @@ def test_orpo_sequence_without_counted_rows_is_nan(flce):
     assert not math.isnan(float(seq[0]))
 
 
+def test_orpo_out_of_range_target_is_nan_not_a_fault(flce):
+    B, T, H, V = 2, 8, 64, 256
+    h, W, t = _inputs(B, T, H, V, seed=59, prompt_max=0, pad_max=0)
+    t[5] = V  # a chosen row of pair 0
+    say("orpo out-of-range target")
+    loss, seq, gh, gw = flce.orpo_fwd_bwd(h.cuda(), W.cuda(), t.cuda(), B, T, 0.1, 1)
+    torch.cuda.synchronize()
+    assert math.isnan(float(loss)) and math.isnan(float(seq[0]))
+    assert not math.isnan(float(seq[1]))
+
+
 def test_orpo_llama2_like_head(flce):
     """A Llama-2-7B-like vocabulary (V = 32000) at H = 1024: 2 pairs of 512
     tokens, one pair per chunk, against the oracle element by element."""
