@@ -297,7 +297,7 @@ size_t flce_vocab_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t vchun
 /*
  * Odds-ratio preference (ORPO) loss over the same head.  Page 2,
  * "Liger-Kernel: Triton kernels that replace Hugging Face training ops",
- * section on installation and use, lists ORPO among the chunked
+ * section "Installation and the one-line patch", lists ORPO among the chunked
  * post-training losses called with the LM-head weight, the hidden states
  * and the targets that return the loss itself; the pages give no formula,
  * so the objective is the published one of ORPO (Hong, Lee and Thorne,

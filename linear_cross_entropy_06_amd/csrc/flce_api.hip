@@ -582,11 +582,11 @@ extern "C" flce_status flce_fwd_bwd_vocab(const void* h, const void* W, const in
 
 // ---------------------------------------------------------------------------
 // Odds-ratio preference loss over the same head (page 2, "Liger-Kernel:
-// Triton kernels that replace Hugging Face training ops", section on
-// installation and use: ORPO is one of the chunked post-training losses
-// called with the LM-head weight, the hidden states and the targets; the
-// objective is the published one, see orpo.hip).  Rows: 2B sequences of T
-// tokens, sequences [0, B) chosen, [B, 2B) rejected.  The batch is worked
+// Triton kernels that replace Hugging Face training ops", section
+// "Installation and the one-line patch": ORPO is one of the chunked
+// post-training losses called with the LM-head weight, the hidden states
+// and the targets; the objective is the published one, see orpo.hip).
+// Rows: 2B sequences of T tokens, sequences [0, B) chosen, [B, 2B) rejected.  The batch is worked
 // through in chunks of Pc pairs; a chunk's chosen and rejected rows are
 // copied next to each other into the workspace, so every pair's two
 // sequences are in one chunk and the head's kernels run unchanged:

@@ -2,10 +2,10 @@
 // per-pair steps between the head's row statistics and its gradient GEMMs.
 //
 // Page 2, "Liger-Kernel: Triton kernels that replace Hugging Face training
-// ops", section on installation and use, lists ORPO among the chunked
-// post-training losses that take the LM-head weight, the hidden states and
-// the targets and return the loss; the objective is the published one of
-// ORPO (Hong, Lee and Thorne, 2024):
+// ops", section "Installation and the one-line patch", lists ORPO among the
+// chunked post-training losses that take the LM-head weight, the hidden
+// states and the targets and return the loss; the objective is the
+// published one of ORPO (Hong, Lee and Thorne, 2024):
 //   l_s      min(mean over the counted rows of sequence s of log p(t_r),
 //            -2^-14)
 //   lo_s     = l_s - ln(1 - exp(l_s))                       (log odds)

@@ -6,9 +6,10 @@ path, with which it shares no code.
 What the pages fix, and what is read into them
 ----------------------------------------------
 Page 2, "Liger-Kernel: Triton kernels that replace Hugging Face training
-ops", section on installation and use: the chunked post-training losses are
-called directly with the LM-head weight, the hidden states and the targets,
-and return the loss itself rather than logits; ORPO is one of them.  The
+ops", section "Installation and the one-line patch": the chunked
+post-training losses are called directly with the LM-head weight, the hidden
+states and the targets, and return the loss itself rather than logits; ORPO
+is one of them.  The
 pages give nothing more, so this module follows the published objective of
 ORPO (Hong, Lee and Thorne, "ORPO: Monolithic Preference Optimization
 without Reference Model", 2024), written out from its definition:
