@@ -23,12 +23,14 @@ ROOT = os.path.dirname(os.path.dirname(HERE))
 sys.path.insert(0, ROOT)
 
 import oracle  # noqa: E402
-from synth import CONFIGS, make_inputs, mask_preference_rows, to_float64  # noqa: E402
+from synth import (CONFIGS, config_by_name, make_inputs, mask_preference_rows,  # noqa: E402
+                   to_float64)
 
 # The preference batch the benchmark times: workload 3's rows as 4 pairs of
 # 1024-token sequences, prompts of up to 256 and padding of up to 128 rows
 # ignored, beta 0.1.
-ORPO = dict(config=3, pairs=4, seq_len=1024, prompt_max=256, pad_max=128, beta=0.1)
+ORPO = dict(workload="llama3_8b_head", pairs=4, seq_len=1024, prompt_max=256, pad_max=128,
+            beta=0.1)
 
 
 def sample_rows(cfg, t: np.ndarray):
@@ -71,7 +73,7 @@ def make(idx: int) -> str:
 
 
 def make_orpo() -> str:
-    cfg = CONFIGS[ORPO["config"]]
+    cfg = config_by_name(ORPO["workload"])
     B, T = ORPO["pairs"], ORPO["seq_len"]
     t0 = time.perf_counter()
     x = make_inputs(cfg, seed=0)

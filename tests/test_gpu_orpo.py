@@ -226,7 +226,7 @@ def test_orpo_full_size_sampled(flce):
     oracle's stored values, plus properties that hold at any size (columns
     of grad_W sum to zero; ignored rows have zero grad_h)."""
     import os
-    from synth import CONFIGS, make_inputs
+    from synth import config_by_name, make_inputs
     p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
                      "orpo_llama3_8b_head_sampled.npz")
     if not os.path.exists(p):
@@ -234,7 +234,7 @@ def test_orpo_full_size_sampled(flce):
     gold = np.load(p, allow_pickle=False)
     B, T, beta = int(gold["pairs"]), int(gold["seq_len"]), float(gold["beta"])
     say("orpo full size: generating inputs")
-    inp = make_inputs(CONFIGS[3], seed=0)
+    inp = make_inputs(config_by_name(str(gold["config"])), seed=0)
     t = mask_preference_rows(inp.t, B, T, seed=0, prompt_max=int(gold["prompt_max"]),
                              pad_max=int(gold["pad_max"]))
     h, W, td = inp.h.cuda(), inp.W.cuda(), t.cuda()
