@@ -17,6 +17,10 @@ per launch (2 * M * N * K flops of one chunk's contraction) / its mean
 launch duration.
 cpu_baseline: the fp64 CPU oracle on the first S tokens of the same
 workload (full V x H head), timed on this host's cores.
+mfma_rate: the MFMA rate and shader clock the part sustains running the
+GEMMs' instruction stream from registers (flce_mfma_rate), with random and
+with zero operands.  pct_measured_mfma_rate relates the step's TFLOP/s to
+the random-operand rate.
 """
 
 from __future__ import annotations
@@ -40,6 +44,44 @@ GEMM_STEPS = ("logits_gemm", "grad_h_gemm", "grad_W_gemm")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3_8b_head.md")
 KERNEL_SOURCES = ("gemm_bf16.hip", "gemm_bf16_dma.hip", "ce_rows.hip", "flce_api.hip",
                   "flce_internal.h")
+
+
+def measure_mfma_rate(flce, torch, dev, iters=40000):
+    """The bf16 MFMA rate and shader clock the part sustains for the GEMMs'
+    instruction stream with no memory traffic (flce_mfma_rate): one
+    256-thread workgroup per CU, 16 32x32x16 MFMAs per round.  It is taken
+    once with random operands drawn like the logits GEMM's (N(0,1) by
+    N(0, 0.02^2) bf16) and once with zero operands, whose inputs do not
+    toggle.  It is timed with events on the current stream."""
+    import numpy as np
+    wg = torch.cuda.get_device_properties(dev).multi_processor_count
+    groups = wg * 4 * 64                      # one 128-byte group per lane
+    g = torch.Generator().manual_seed(11)
+    a = torch.randn(groups, 32, generator=g)
+    b = 0.02 * torch.randn(groups, 32, generator=g)
+    cases = {"random": torch.cat([a, b], 1).to(torch.bfloat16).to(dev),
+             "zero": torch.zeros(groups, 64, dtype=torch.bfloat16, device=dev)}
+    out = {}
+    for name, ops in cases.items():
+        flce.mfma_rate(ops, iters // 10, wg)  # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _, clocks = flce.mfma_rate(ops, iters, wg)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        c = clocks.cpu().double().numpy()
+        flop = wg * 4.0 * iters * 16 * 32768
+        out[name] = {"tflops": flop / (ms * 1e-3) / 1e12,
+                     "clock_ghz": float(np.median(c[:, 0] / (c[:, 1] * 10.0))),
+                     "ms": ms}
+    return {"operands": "bf16, N(0,1) x N(0,0.02^2) (random) and all zero",
+            "workgroups": wg, "iters": iters,
+            "flop_per_call": wg * 4.0 * iters * 16 * 32768,
+            "random_tflops": out["random"]["tflops"],
+            "random_clock_ghz": out["random"]["clock_ghz"],
+            "zero_tflops": out["zero"]["tflops"],
+            "zero_clock_ghz": out["zero"]["clock_ghz"]}
 
 
 def parse_args():
@@ -541,6 +583,8 @@ def main() -> int:
     achieved = flop_per_launch / (avg_ms[dominant] * 1e-3) / 1e12
     traffic = read_traffic(dominant, cfg.name)
 
+    mfma = measure_mfma_rate(flce, torch, dev)
+
     loss_val = float(loss)
     gold = os.path.join(ROOT, "tests", "golden", f"cfg{cfg.idx}_sampled.npz")
     loss_ref = float(np.load(gold)["loss"]) if os.path.exists(gold) and args.seed == 0 else None
@@ -562,6 +606,8 @@ def main() -> int:
                    "seed": args.seed},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "pct_measured_mfma_rate": 100.0 * tflops / mfma["random_tflops"],
+        "mfma_rate": mfma,
         "workspace_bytes": ws_bytes,
         "naive_logits_bytes": cfg.naive_logits_bytes,
         "workspace_frac_of_naive": ws_bytes / cfg.naive_logits_bytes,

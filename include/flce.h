@@ -353,6 +353,40 @@ flce_status flce_orpo_fwd_bwd(const void* h, const void* W, const int32_t* targe
 size_t flce_orpo_workspace_bytes(int64_t pairs, int64_t seq_len, int64_t H, int64_t V,
                                  int64_t chunk_pairs, flce_dtype dt);
 
+/*
+ * Matrix-core rate microbenchmark.  This is a measurement aid, not a step
+ * of the loss: it gives the bf16 MFMA rate and shader clock the part
+ * sustains when it runs the contractions' instruction stream with no memory
+ * traffic.  The loss head's GEMMs are compared against that ceiling as well
+ * as against the published dense peak.
+ *
+ * It launches `workgroups` workgroups of 4 waves, one wave per SIMD as in
+ * the head's GEMMs.  Each wave loads eight 16-byte operand fragments once.
+ * Lane l of wave w reads the 128-byte group g = (w*64 + l) mod G, where
+ * G = min(floor(operand_bytes / 128), 2^30); the group's pieces 0-3 are its
+ * A fragments and pieces 4-7 its B fragments.  It then runs `iters`
+ * rounds of the 4 x 4 products acc[i][j] += A_i B_j^T, each one
+ * v_mfma_f32_32x32x16_bf16: 32x16 by 16x32 blocks, with lane l holding
+ * row (or column) l % 32 and k = 8*(l/32) .. 8*(l/32)+7 of its block.
+ * One call performs workgroups * 4 * iters * 16 * 32768 flop.
+ * Outputs, per wave w = 4 * workgroup + wave index:
+ *   sink[w]          fp32 sum, over the wave's 64 lanes and 16 blocks, of
+ *                    each lane's element 0 of the block: row 4*(l/32),
+ *                    column l % 32 of that block's 32x32 result;
+ *   clocks[2w]       shader clocks the wave spent in its loop (s_memtime);
+ *   clocks[2w + 1]   ticks of the constant-rate reference counter
+ *                    (s_memrealtime, 100 MHz) over the same interval.
+ *                    Their ratio is the wave's clock.
+ * Requires: operands 16-byte aligned with operand_bytes >= 8192 and a
+ * multiple of 16; sink [4 * workgroups] fp32 (4-byte aligned); clocks
+ * [8 * workgroups] uint64 (8-byte aligned); 1 <= iters <= 2^40;
+ * 1 <= workgroups <= 65535.  Otherwise it returns INVALID_ARG or
+ * UNSUPPORTED and enqueues nothing.
+ */
+flce_status flce_mfma_rate(const void* operands, int64_t operand_bytes, int64_t iters,
+                           int64_t workgroups, float* sink, uint64_t* clocks,
+                           hipStream_t stream);
+
 /* A static, human-readable name for a status code (host only). */
 const char* flce_status_string(flce_status s);
 

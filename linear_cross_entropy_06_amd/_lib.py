@@ -46,6 +46,7 @@ EXPORTS = (
     "flce_rmsnorm_workspace_bytes",
     "flce_orpo_fwd_bwd",
     "flce_orpo_workspace_bytes",
+    "flce_mfma_rate",
     "flce_status_string",
 )
 
@@ -107,6 +108,8 @@ def load() -> ctypes.CDLL:
     lib.flce_orpo_fwd_bwd.restype = ctypes.c_int
     lib.flce_orpo_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int]
     lib.flce_orpo_workspace_bytes.restype = sz
+    lib.flce_mfma_rate.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+    lib.flce_mfma_rate.restype = ctypes.c_int
     lib.flce_status_string.argtypes = [ctypes.c_int]
     lib.flce_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -441,6 +444,28 @@ def scale_grads(grad_h: Optional[torch.Tensor], grad_W: Optional[torch.Tensor],
             raise TypeError("grad_W must be float32")
         pw, nw = grad_W.data_ptr(), grad_W.numel()
     _check(lib.flce_scale_grads(ph, nh, pw, nw, scale.data_ptr(), dt, _stream_ptr(dev)))
+
+
+def mfma_rate(operands: torch.Tensor, iters: int, workgroups: int
+              ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Matrix-core rate microbenchmark (``flce_mfma_rate``): ``workgroups``
+    x 4 waves each run ``iters`` rounds of 16 bf16 32x32x16 MFMAs on
+    fragments taken from ``operands`` (a contiguous GPU tensor of at least
+    8 KiB, whole 16-byte pieces).  Returns (sink [4 * workgroups] fp32: per
+    wave, the sum over its lanes l and 16 blocks of the block's result at
+    row 4 * (l // 32), column l % 32; clocks [4 * workgroups, 2] int64: the
+    shader clocks and 100 MHz reference ticks each wave spent in its loop)."""
+    lib = load()
+    _need_cuda(operands)
+    if not operands.is_contiguous():
+        raise ValueError("operands must be contiguous")
+    dev = operands.device
+    nbytes = operands.numel() * operands.element_size()
+    sink = torch.empty(4 * workgroups, dtype=torch.float32, device=dev)
+    clocks = torch.empty((4 * workgroups, 2), dtype=torch.int64, device=dev)
+    _check(lib.flce_mfma_rate(operands.data_ptr(), nbytes, int(iters), int(workgroups),
+                              sink.data_ptr(), clocks.data_ptr(), _stream_ptr(dev)))
+    return sink, clocks
 
 
 class LinearCrossEntropyFunction(torch.autograd.Function):

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["flce_api.hip", "gemm_bf16.hip", "gemm_bf16_dma.hip", "gemm_f32.hip", "ce_rows.hip",
-           "grad_scale.hip", "rmsnorm.hip", "orpo.hip"]
+           "grad_scale.hip", "rmsnorm.hip", "orpo.hip", "mfma_rate.hip"]
 
 
 def hipcc() -> str:

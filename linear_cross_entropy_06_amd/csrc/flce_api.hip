@@ -760,6 +760,27 @@ extern "C" flce_status flce_orpo_fwd_bwd(const void* h, const void* W, const int
              : FLCE_ERR_HIP;
 }
 
+extern "C" flce_status flce_mfma_rate(const void* operands, int64_t operand_bytes,
+                                     int64_t iters, int64_t workgroups, float* sink,
+                                     uint64_t* clocks, hipStream_t stream) {
+  if (!operands || !sink || !clocks) return FLCE_ERR_INVALID_ARG;
+  if (operand_bytes < 8192 || operand_bytes % 16 != 0 || iters < 1 ||
+      iters > (int64_t{1} << 40) || workgroups < 1 || workgroups > 65535)
+    return FLCE_ERR_INVALID_ARG;
+  if (!aligned16(operands) || (reinterpret_cast<uintptr_t>(sink) & 3u) ||
+      (reinterpret_cast<uintptr_t>(clocks) & 7u))
+    return FLCE_ERR_UNSUPPORTED;
+  const int64_t groups = operand_bytes / 128;
+  return flce::launch_mfma_rate(operands,
+                                static_cast<int>(groups < (int64_t{1} << 30) ? groups
+                                                                             : int64_t{1} << 30),
+                                iters,
+                                static_cast<int>(workgroups), sink, clocks,
+                                stream) == hipSuccess
+             ? FLCE_OK
+             : FLCE_ERR_HIP;
+}
+
 extern "C" const char* flce_status_string(flce_status s) {
   switch (s) {
     case FLCE_OK: return "FLCE_OK";

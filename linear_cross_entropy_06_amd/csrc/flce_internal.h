@@ -167,4 +167,13 @@ hipError_t launch_loss_sum(const float* row_loss, int64_t loss_stride,
                            int rows, float scale, int first, float* loss,
                            hipStream_t s);
 
+// Matrix-core rate microbenchmark (mfma_rate.hip): `workgroups` x 4 waves,
+// each running `iters` rounds of 16 v_mfma_f32_32x32x16_bf16 on fragments
+// read from the first n_groups 128-byte groups at ops (16-byte aligned);
+// per wave w, sink[w] = sum of element 0 of its 16 accumulator blocks over
+// its lanes, clocks[2w] = shader clocks
+// and clocks[2w + 1] = reference-counter ticks spent in the loop.
+hipError_t launch_mfma_rate(const void* ops, int n_groups, int64_t iters, int workgroups,
+                            float* sink, uint64_t* clocks, hipStream_t s);
+
 }  // namespace flce

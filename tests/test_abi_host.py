@@ -42,7 +42,8 @@ def test_header_declares_the_boundary():
                             "flce_cross_entropy", "flce_fwd_bwd_vocab",
                             "flce_vocab_workspace_bytes", "flce_fwd_bwd_rmsnorm",
                             "flce_rmsnorm_workspace_bytes", "flce_orpo_fwd_bwd",
-                            "flce_orpo_workspace_bytes", "flce_status_string"])
+                            "flce_orpo_workspace_bytes", "flce_mfma_rate",
+                            "flce_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -340,6 +341,22 @@ def test_workspace_sizes_that_would_overflow_are_refused(lib):
     assert st == UNSUPPORTED
     assert _ocall(lib, B=2 ** 28, T=2, V=big - 7, cp=2 ** 28, wsb=1 << 62) == INVALID
     # (the vocabulary-chunked path needs H, V < 2^22, so its areas stay below 2^53)
+
+
+def test_mfma_rate_validates(lib):
+    f = lib.flce_mfma_rate
+    assert f(None, 8192, 10, 256, P, P, None) == INVALID          # no operands
+    assert f(P, 8192, 10, 256, None, P, None) == INVALID          # no sink
+    assert f(P, 8192, 10, 256, P, None, None) == INVALID          # no clocks
+    assert f(P, 8176, 10, 256, P, P, None) == INVALID             # below one wave's pieces
+    assert f(P, 8200, 10, 256, P, P, None) == INVALID             # not whole pieces
+    assert f(P, 8192, 0, 256, P, P, None) == INVALID              # iterations
+    assert f(P, 8192, 2 ** 40 + 1, 256, P, P, None) == INVALID
+    assert f(P, 8192, 10, 0, P, P, None) == INVALID               # workgroups
+    assert f(P, 8192, 10, 65536, P, P, None) == INVALID
+    assert f(P + 8, 8192, 10, 256, P, P, None) == UNSUPPORTED     # alignment
+    assert f(P, 8192, 10, 256, P + 2, P, None) == UNSUPPORTED
+    assert f(P, 8192, 10, 256, P, P + 4, None) == UNSUPPORTED
 
 
 def test_status_strings(lib):

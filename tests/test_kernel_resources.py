@@ -24,9 +24,9 @@ CSRC = os.path.join(ROOT, "linear_cross_entropy_06_amd", "csrc")
 HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
 
 SOURCES = ["gemm_bf16_dma.hip", "gemm_bf16.hip", "gemm_f32.hip", "ce_rows.hip",
-           "grad_scale.hip", "rmsnorm.hip", "orpo.hip", "flce_api.hip"]
+           "grad_scale.hip", "rmsnorm.hip", "orpo.hip", "mfma_rate.hip", "flce_api.hip"]
 FUSED = ["gemm_bf16_dma.hip", "gemm_f32.hip", "ce_rows.hip", "grad_scale.hip", "rmsnorm.hip",
-         "orpo.hip"]
+         "orpo.hip", "mfma_rate.hip"]
 
 
 def _report(src, out):
