@@ -289,6 +289,7 @@ def bench_vocab(args) -> int:
     ev_ms = e0.elapsed_time(e1) / args.steps
     head_flops = 6.0 * N * V * H
     run_flops = 8.0 * N * V * H
+    mfma = measure_mfma_rate(flce, torch, h.device)
     out = {
         "metric": "FLCE fwd+bwd tokens/s (vocabulary-chunked entry point)",
         "value": N / (ms * 1e-3), "unit": "tokens/s",
@@ -299,6 +300,8 @@ def bench_vocab(args) -> int:
                    "seed": args.seed},
         "head_tflops": head_flops / (ms * 1e-3) / 1e12,
         "executed_tflops": run_flops / (ms * 1e-3) / 1e12,
+        "pct_measured_mfma_rate": 100.0 * run_flops / (ms * 1e-3) / 1e12 / mfma["random_tflops"],
+        "mfma_rate": mfma,
         "workspace_bytes": need,
         "naive_logits_bytes": N * V * 4,
         "token_chunk_workspace_bytes_c4096": flce.workspace_bytes(N, H, V, 4096, h.dtype),
@@ -373,6 +376,7 @@ def bench_rmsnorm(args) -> int:
     ms = (t1 - t0) * 1e3 / args.steps
     ev_ms = e0.elapsed_time(e1) / args.steps
     flops = 6.0 * N * V * H
+    mfma = measure_mfma_rate(flce, torch, x.device)
     out = {
         "metric": "FLCE fwd+bwd tokens/s (behind an RMSNorm, flce_fwd_bwd_rmsnorm)",
         "value": N / (ms * 1e-3), "unit": "tokens/s",
@@ -382,6 +386,8 @@ def bench_rmsnorm(args) -> int:
         "config": {"workload": cfg.name, "N": N, "H": H, "V": V, "chunk": C, "eps": 1e-6,
                    "seed": args.seed},
         "tflops": flops / (ms * 1e-3) / 1e12,
+        "pct_measured_mfma_rate": 100.0 * flops / (ms * 1e-3) / 1e12 / mfma["random_tflops"],
+        "mfma_rate": mfma,
         "workspace_bytes": need,
         "loss": loss0,
         "roofline": {
@@ -450,6 +456,7 @@ def bench_orpo(args) -> int:
     ms = (t1 - t0) * 1e3 / args.steps
     ev_ms = e0.elapsed_time(e1) / args.steps
     flops = 6.0 * N * V * H
+    mfma = measure_mfma_rate(flce, torch, h.device)
     out = {
         "metric": "ORPO over the fused head, fwd+bwd tokens/s",
         "value": N / (ms * 1e-3), "unit": "tokens/s",
@@ -461,6 +468,8 @@ def bench_orpo(args) -> int:
                    "chunk_pairs": cp, "beta": beta, "seed": args.seed},
         "counted_rows": int((t_cpu >= 0).sum()),
         "tflops": flops / (ms * 1e-3) / 1e12,
+        "pct_measured_mfma_rate": 100.0 * flops / (ms * 1e-3) / 1e12 / mfma["random_tflops"],
+        "mfma_rate": mfma,
         "workspace_bytes": need,
         "naive_logits_bytes": N * V * 4,
         "loss": loss0,
