@@ -153,11 +153,22 @@ def cpu_baseline(inp, cfg, sample_tokens: int, chunk: int):
     t0 = time.perf_counter()
     loss, _, _ = oracle.flce_chunked(h64, W64, t, chunk)
     dt = time.perf_counter() - t0
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                              if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    blas = sorted({f"{d.get('internal_api')} {d.get('version')}" for d in threadpool_info()
+                   if d.get("user_api") == "blas"})
     return {
         "value": S / dt,
         "unit": "tokens/s",
         "cores": int(blas_threads),
         "kind": "oracle",
+        "cpu_model": cpu_model,
+        "blas": ", ".join(blas) or None,
         "sample": (f"first {S} of {cfg.N} tokens of {cfg.name} against the full "
                    f"{cfg.V}x{cfg.H} head, fp64 numpy oracle, token chunk {chunk}: "
                    f"{dt:.2f} s for {6.0 * S * cfg.V * cfg.H / 1e12:.2f} TFLOP "
@@ -622,6 +633,7 @@ def main() -> int:
         "workspace_frac_of_naive": ws_bytes / cfg.naive_logits_bytes,
         "hidden_alloc_bytes": int(hidden_alloc),
         "gpu_ms_per_step_events": float(np.median(gpu_ms)),
+        "gpu_ms_per_step_events_min": float(np.min(gpu_ms)),
         "kernel_ms_per_launch": avg_ms,
         "kernel_share": {k: v / sum(tot_ms.values()) for k, v in tot_ms.items()},
         "loss": loss_val,
