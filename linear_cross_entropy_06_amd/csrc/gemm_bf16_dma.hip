@@ -26,7 +26,15 @@
 //                    block as sixteen 8-byte pieces and each lane receives
 //                    4 consecutive k of one m, i.e. an MFMA operand slice.
 //    16-byte chunks are XOR-swizzled per row (the DMA source address is
-//    permuted to match) so fragment reads hit distinct LDS banks.
+//    permuted to match) so fragment reads hit distinct LDS banks.  The LDS
+//    has 64 four-byte banks (256 B a cycle).  A k-contiguous row is 128 B,
+//    so rows r and r + 1 fill the two bank halves.  XOR-ing the chunk with
+//    (r >> 1) & 7 gives the 16 consecutive rows of a ds_read_b128 lane group
+//    16 distinct (half, chunk) positions.  XOR-ing with r & 7 left rows r
+//    and r + 8 on the same banks, a 2-way conflict measured at 2-3% of the
+//    GEMM time.  An m-contiguous row is 512 B; its XOR,
+//    4 (k & 3) ^ 2 ((k >> 3) & 1) of k-row k, makes lane groups 0/1, 2/3,
+//    0/2 and 1/3 of a ds_read_b64_tr_b16 cover complementary bank sets.
 //  * MFMA operands are double-buffered in registers: the fragments of the
 //    next 16-wide k step are read while the current step's 16 MFMAs run.
 //  * Tiles are walked in groups of 4 row panels (each XCD's ~32 concurrent
@@ -131,14 +139,14 @@ struct DmaOperand {
       if constexpr (KC) {
         // 8 rows of 64 k (128 B) per block; 8 chunks per row.
         const int row = 8 * b + (lane >> 3);
-        const int c = (lane & 7) ^ (row & 7);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);  // bank swizzle, see the header
         int grow = row0 + row;
         grow = grow < rows_total ? grow : rows_total - 1;
         elem = (int64_t)(grow - row0) * ld + 8 * c;
       } else {
         // 2 k-rows of 256 m (512 B) per block; 32 chunks per row.
         const int krow = 2 * b + (lane >> 5);
-        const int c = (lane & 31) ^ (2 * (krow & 3));
+        const int c = (lane & 31) ^ (4 * (krow & 3) ^ 2 * ((krow >> 3) & 1));  // see the header
         int gm = row0 + 8 * c;
         gm = gm <= rows_total - 8 ? gm : rows_total - 8;
         elem = (int64_t)krow * ld + (gm - row0);
@@ -172,7 +180,7 @@ struct FragOperand {
     if constexpr (KC) {
       // row = wrow0 + 32 i + (lane & 31); chunk = 2 kk + (lane >> 5).
       const int row = wrow0 + (lane & 31);
-      const int x = row & 7;
+      const int x = (row >> 1) & 7;
       const int h = lane >> 5;
 #pragma unroll
       for (int kk = 0; kk < kKSteps; ++kk) off[kk] = row * 128 + (((2 * kk + h) ^ x) * 16);
@@ -181,7 +189,7 @@ struct FragOperand {
       // m = 16 (G & 1) + 4 (j & 3) .. + 3 of each 32-row block.
       const int G = lane >> 4, j = lane & 15;
       const int krow = 8 * (G >> 1) + (j >> 2);
-      const int x = 2 * (krow & 3);
+      const int x = 4 * (krow & 3) ^ 2 * ((krow >> 3) & 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = wrow0 + 32 * i + 16 * (G & 1) + 4 * (j & 3);
