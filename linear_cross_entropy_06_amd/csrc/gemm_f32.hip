@@ -4,14 +4,19 @@
 // B(n,k), stored as out[n * ldo + m]); used for fp32 operands, where the
 // path is small and fp32 FMA on the vector ALUs reaches the same peak as the
 // fp32 matrix instructions.  64x64 output tile per 256-thread workgroup, each
-// thread a 4x4 register block, K walked in 16-wide slabs staged in LDS in
-// [k][row] order so the inner loop reads broadcast-free float4s.
+// thread a 4x4 register block, K walked in 32-wide slabs staged in LDS in
+// [k][row] order so the inner loop reads broadcast-free float4s.  The next
+// slab's operands are loaded into registers while the current slab's FMAs
+// run: at the head's fp32 shapes the grid is a few workgroups with a long K
+// (grad_h of 256 tokens: 8 tiles, K = V), so each slab's memory round trip,
+// not arithmetic, sets the time.
 #include "flce_internal.h"
 
 namespace flce {
 namespace {
 
-constexpr int kBM = 64, kBN = 64, kBK = 16, kNT = 256;
+constexpr int kBM = 64, kBN = 64, kBK = 32, kNT = 256;
+constexpr int kLA = (kBM * kBK) / kNT, kLB = (kBN * kBK) / kNT;  // loads per thread and slab
 
 template <bool KC>
 __device__ __forceinline__ float ld_op(const float* __restrict__ p, int64_t ld, int row,
@@ -32,24 +37,44 @@ __global__ void __launch_bounds__(kNT) gemm_f32_kernel(GemmArgs g) {
   const float* __restrict__ B = static_cast<const float*>(g.B);
   const int tx = tid % 16, ty = tid / 16;
 
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < g.K; k0 += kBK) {
+  // Element i of a thread's share of a slab: tile row r, slab column k.
+  // k-contiguous operands: consecutive threads walk k; otherwise rows.
+  float ra[kLA], rb[kLB];
+  auto fetch = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < (kBM * kBK) / kNT; ++i) {
+    for (int i = 0; i < kLA; ++i) {
       const int q = tid + kNT * i;
-      // k-contiguous operands: consecutive threads walk k; otherwise rows.
       const int r = A_KC ? q / kBK : q % kBM;
       const int k = A_KC ? q % kBK : q / kBM;
-      As[k][r] = ld_op<A_KC>(A, g.lda, m0 + r, g.M, k0 + k, g.K);
+      ra[i] = ld_op<A_KC>(A, g.lda, m0 + r, g.M, k0 + k, g.K);
     }
 #pragma unroll
-    for (int i = 0; i < (kBN * kBK) / kNT; ++i) {
+    for (int i = 0; i < kLB; ++i) {
       const int q = tid + kNT * i;
       const int r = B_KC ? q / kBK : q % kBN;
       const int k = B_KC ? q % kBK : q / kBN;
-      Bs[k][r] = ld_op<B_KC>(B, g.ldb, n0 + r, g.N, k0 + k, g.K);
+      rb[i] = ld_op<B_KC>(B, g.ldb, n0 + r, g.N, k0 + k, g.K);
     }
+  };
+  auto stage = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kLA; ++i) {
+      const int q = tid + kNT * i;
+      As[A_KC ? q % kBK : q / kBM][A_KC ? q / kBK : q % kBM] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kLB; ++i) {
+      const int q = tid + kNT * i;
+      Bs[B_KC ? q % kBK : q / kBN][B_KC ? q / kBK : q % kBN] = rb[i];
+    }
+  };
+
+  float acc[4][4] = {};
+  fetch(0);
+  for (int k0 = 0; k0 < g.K; k0 += kBK) {
+    stage();
     __syncthreads();
+    if (k0 + kBK < g.K) fetch(k0 + kBK);  // in flight during this slab's FMAs
 #pragma unroll
     for (int k = 0; k < kBK; ++k) {
       float a[4], b[4];
