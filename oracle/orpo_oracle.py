@@ -20,8 +20,7 @@ without Reference Model", 2024), written out from its definition:
     counted     a row counts when its target is >= 0 (a negative target
                 marks a prompt or padding position)
     log p_r     = Z[r, t_r] - lse_r,  Z = h W^T             (per counted row)
-    l_s         = min(mean of log p_r over the counted rows of sequence s,
-                      -2^-14)
+    l_s         = mean of log p_r over the counted rows of sequence s
     logodds_s   = l_s - ln(1 - exp(l_s))
     L_OR        = -(1/B) sum_b ln sigmoid(logodds_b - logodds_{B+b})
     L_SFT       = -(1/M) sum of log p_r over the counted chosen rows
@@ -36,19 +35,17 @@ of pair b,
     c_r = 1/M [chosen only] + beta/B * sigmoid(-(lo_b - lo_{B+b}))
           * (+1 chosen, -1 rejected) / ((1 - exp(l_s)) n_s)
 
-with n_s the counted rows of the row's sequence s, and no odds-ratio part
-for a sequence whose mean sits at the floor.  A sequence with no counted
-row has no mean log-probability; the result is then NaN.
+with n_s the counted rows of the row's sequence s.  A sequence with no
+counted row has no mean log-probability; the result is then NaN.
 
-The floor -2^-14 on l_s is a reading of this build, not the paper's: as a
-sequence becomes certain (every token's probability near 1) l_s -> 0 and
-ln(1 - exp(l_s)) -> -inf, and in fp32 a per-token log-probability (the
-difference of a log-sum-exp and a target logit) carries an absolute error of
-about one unit in the last place of the logits, 2^-18 to 2^-16 for logits of
-magnitude 30 to 100, so a mean above the floor is not resolvable and may
-even round to >= 0.  At the floor the odds-ratio term is constant in
-that sequence's log-probabilities (the derivative of the min), so such a
-sequence still gets its SFT gradient and a finite loss.
+A confident model needs the digits of 1 - p: the odds divide by
+1 - exp(l), tiny when every token is near certain.  So when Z[r, t_r] is
+the row's largest logit, log p_r is evaluated as
+-log1p(sum over j != t_r of exp(Z[r, j] - Z[r, t_r])), the same number in
+exact arithmetic as lse - Z_t, whose difference loses the small sum to
+rounding; 1 - exp(l) is -expm1(l) and p_t - 1 in the gradient is
+expm1(log p_t).  The objective has no floor: in fp64 these stay finite and
+nonzero up to logit margins of several hundred.
 """
 
 from __future__ import annotations
@@ -57,15 +54,26 @@ import math
 
 import numpy as np
 
-# Upper bound of a sequence's mean log-probability (see the module notes).
-LOGP_FLOOR = -(2.0 ** -14)
-
 
 def _split(t: np.ndarray, pairs: int, seq_len: int):
     t = np.asarray(t)
     if t.shape != (2 * pairs * seq_len,):
         raise ValueError("targets must hold 2 * pairs * seq_len rows")
     return t.reshape(2 * pairs, seq_len)
+
+
+def _target_logp(Z: np.ndarray, t: np.ndarray, lse: np.ndarray) -> np.ndarray:
+    """log softmax(Z)[r, t_r] for rows of Z with targets t: lse - Z_t, or,
+    when Z_t is the row's largest logit, -log1p of the other classes'
+    relative mass (the same value, without the cancellation)."""
+    k = np.arange(Z.shape[0])
+    zt = Z[k, t]
+    D = Z - zt[:, None]
+    D[k, t] = -np.inf
+    top = D.max(axis=1) <= 0.0
+    with np.errstate(over="ignore"):
+        S = np.exp(D).sum(axis=1)
+    return np.where(top, -np.log1p(np.where(top, S, 0.0)), zt - lse)
 
 
 def token_logp(h: np.ndarray, W: np.ndarray, t: np.ndarray):
@@ -84,7 +92,7 @@ def token_logp(h: np.ndarray, W: np.ndarray, t: np.ndarray):
     counted = t >= 0
     logp = np.zeros(h.shape[0])
     rows = np.nonzero(counted)[0]
-    logp[rows] = Z[rows, t[rows]] - lse[rows]
+    logp[rows] = _target_logp(Z[rows], t[rows], lse[rows])
     return logp, P, counted
 
 
@@ -97,24 +105,21 @@ def objective(logp: np.ndarray, counted: np.ndarray, pairs: int, seq_len: int,
     lp = logp.reshape(2 * B, T)
     cnt = counted.reshape(2 * B, T).sum(axis=1).astype(np.float64)
     with np.errstate(divide="ignore", invalid="ignore"):
-        l_raw = lp.sum(axis=1) / cnt                     # mean log p per sequence
-        at_floor = l_raw > LOGP_FLOOR                    # False for NaN
-        l_seq = np.where(at_floor, LOGP_FLOOR, l_raw)
-        logodds = l_seq - np.log1p(-np.exp(l_seq))       # ln(P / (1 - P))
+        l_seq = lp.sum(axis=1) / cnt                     # mean log p per sequence
+        Q = -np.expm1(l_seq)                             # 1 - exp(l)
+        logodds = l_seq - np.log(Q)                      # ln(P / (1 - P))
     ratio = logodds[:B] - logodds[B:]
     # -ln sigmoid(x) = ln(1 + exp(-x)), written stably
     with np.errstate(invalid="ignore"):
         l_or = float(np.mean(np.logaddexp(0.0, -ratio)))
+    sig_neg = 1.0 / (1.0 + np.exp(ratio))                # sigmoid(-ratio)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        per_seq = beta / B * np.concatenate([sig_neg, -sig_neg]) / (Q * cnt)
     M = float(counted[: B * T].sum())
     l_sft = float(-logp[: B * T].sum() / M) if M > 0 else math.nan
     loss = l_sft + beta * l_or
 
     # c_r = -dloss/dlog p_r
-    sig_neg = 1.0 / (1.0 + np.exp(ratio))                # sigmoid(-ratio)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        per_seq = beta / B * np.concatenate([sig_neg, -sig_neg]) / (
-            (1.0 - np.exp(l_seq)) * cnt)
-    per_seq = np.where(at_floor, 0.0, per_seq)
     c = np.repeat(per_seq, T)
     c[: B * T] += 1.0 / M if M > 0 else math.nan
     c = np.where(counted, c, 0.0)
@@ -132,7 +137,7 @@ def orpo(h, W, t, pairs: int, seq_len: int, beta: float):
     loss, c, l_seq = objective(logp, counted, pairs, seq_len, beta)
     G = P
     rows = np.nonzero(counted)[0]
-    G[rows, t[rows]] -= 1.0
+    G[rows, t[rows]] = np.expm1(logp[rows])  # p_t - 1, with its digits near p_t = 1
     G *= c[:, None]
     return loss, G @ W, G.T @ h, l_seq
 
@@ -163,7 +168,7 @@ def orpo_sampled(h, W, t, pairs: int, seq_len: int, beta: float, rows=(), vocab_
         m = Z.max(axis=1, keepdims=True)
         lse[r0:r1] = (m + np.log(np.exp(Z - m).sum(axis=1, keepdims=True)))[:, 0]
         k = np.nonzero(counted[r0:r1])[0]
-        logp[r0 + k] = Z[k, t[r0 + k]] - lse[r0 + k]
+        logp[r0 + k] = _target_logp(Z[k], t[r0 + k], lse[r0 + k])
         del Z
     loss, c, l_seq = objective(logp, counted, pairs, seq_len, beta)
     gh = np.zeros((rows.size, h.shape[1]))
@@ -171,12 +176,13 @@ def orpo_sampled(h, W, t, pairs: int, seq_len: int, beta: float, rows=(), vocab_
         Zr = h[rows] @ W.T
         Gr = np.exp(Zr - lse[rows, None])
         k = np.nonzero(counted[rows])[0]
-        Gr[k, t[rows[k]]] -= 1.0
+        Gr[k, t[rows[k]]] = np.expm1(logp[rows[k]])  # p_t - 1
         gh = (Gr * c[rows, None]) @ W
     gw = np.zeros((vocab_rows.size, h.shape[1]))
     if vocab_rows.size:
         GJ = np.exp(h @ W[vocab_rows].T - lse[:, None])
-        GJ -= (t[:, None] == vocab_rows[None, :])
+        r, j = np.nonzero(t[:, None] == vocab_rows[None, :])
+        GJ[r, j] = np.expm1(logp[r])  # p_t - 1 where the column is the row's target
         gw = (GJ * c[:, None]).T @ h
     return {"loss": loss, "seq_logp": l_seq, "lse": lse, "grad_h_rows": gh,
             "grad_W_rows": gw}

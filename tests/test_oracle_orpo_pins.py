@@ -14,9 +14,13 @@ Facts that do not come from the oracle's own code:
   changes nothing and their grad_h rows are zero;
 * swapping the chosen and rejected halves changes the odds-ratio term by
   the mean log odds ratio (ln sigmoid(x) - ln sigmoid(-x) = x);
-* a sequence the model is certain of (every token's probability 1 - 1e-17)
-  sits at the floor of the mean log-probability: the loss and gradients stay
-  finite and equal torch's (its formulation clamps the mean the same way).
+* two-valued logits (a token's target logit m, every other logit 0): then
+  p = 1 / (1 + (V - 1) e^-m) and the odds p / (1 - p) = e^m / (V - 1)
+  exactly, so the log odds are m - ln(V - 1), the odds ratio of a pair is
+  the difference of its two margins, and the loss, every sequence's mean
+  log-probability and every entry of grad_h have closed forms, also for a
+  sequence the model is certain of (margin 40: 1 - p ~ 1e-17, far below
+  what lse - Z_t resolves in fp64).
 ``test_orpo_mutants_are_caught`` plants plausible mistakes in copies and
 checks that a pin rejects each.
 """
@@ -47,9 +51,6 @@ def _close(a, b, rtol=1e-10, atol=1e-13):
     assert np.allclose(a, b, rtol=rtol, atol=atol), float(np.max(np.abs(a - b)))
 
 
-FLOOR = -(2.0 ** -14)
-
-
 def _torch_ref(h, W, t, B, T, beta):
     """torch fp64: the objective in torch's own ops, gradients by autograd."""
     ht = torch.tensor(h, requires_grad=True)
@@ -60,7 +61,6 @@ def _torch_ref(h, W, t, B, T, beta):
     mask = tt >= 0
     tok = lsm.gather(1, tt.clamp(min=0)[:, None])[:, 0] * mask
     mean_lp = tok.view(2 * B, T).sum(dim=1) / mask.view(2 * B, T).sum(dim=1)
-    mean_lp = torch.clamp(mean_lp, max=FLOOR)
     lo = mean_lp - torch.log(-torch.expm1(mean_lp))
     l_or = -torch.nn.functional.logsigmoid(lo[:B] - lo[B:]).mean()
     l_sft = torch.nn.functional.cross_entropy(z[: B * T], tt[: B * T], ignore_index=-100)
@@ -166,27 +166,60 @@ def pin_swap_halves(impl):
     assert abs(lhs - beta * mean_ratio) <= 1e-11, (lhs, mean_ratio)
 
 
-def pin_certain_sequence(impl):
-    """Chosen sequence 0 certain: W = 5 I, its rows h = 8 e_t, so each of its
-    tokens has logit margin 40 and log p ~ -1e-17 (mean above the floor)."""
-    B, T, V, beta = 2, 3, 5, 0.8
-    h, _, t = _rand(B, T, V, V, seed=10, ignore=(8,))
-    W = 5.0 * np.eye(V)
-    for r in range(T):
-        h[r] = 0.0
-        h[r, t[r]] = 8.0
-    loss, gh, gw, seq = impl(h, W, t, B, T, beta)
-    assert np.isfinite(loss) and np.all(np.isfinite(gh)) and np.all(np.isfinite(gw))
-    assert seq[0] == FLOOR
-    lt, gh_t, gw_t, seq_t = _torch_ref(h, W, t, B, T, beta)
-    assert abs(loss - lt) <= 1e-12 * max(1.0, abs(lt))
-    _close(seq, seq_t)
-    _close(gh, gh_t)
-    _close(gw, gw_t)
+def pin_two_valued(impl):
+    """Closed forms for two-valued logits.  W is the identity in the first V
+    columns and a counted row of sequence s is h_r = m_s e_{t_r}, so its
+    logits are m_s at the target and 0 elsewhere.  Pair b has margins
+    (a_b, b_b) for its chosen and rejected sequence; with q(m) = 1 - p =
+    (V-1) e^-m / (1 + (V-1) e^-m):
+      log p = -log1p((V-1) e^-m),   log odds = m - ln(V-1),
+      loss  = (1/M) sum over counted chosen rows of log1p((V-1) e^-a_b)
+              + (beta/B) sum_b ln(1 + e^(b_b - a_b)),
+      dloss/dZ[r, t_r] = -q(a_b)/M - (beta/B) sigmoid(b_b - a_b) / n_w   (chosen)
+                       = +(beta/B) sigmoid(b_b - a_b) / n_l              (rejected),
+    and the V - 1 other logits of the row share -(that) / (V - 1) (the row
+    of G sums to zero); grad_h = G W is G itself in the first V columns."""
+    V, H, T, beta = 6, 8, 4, 0.6
+    margins = [(40.0, 10.0), (10.0, 40.0), (12.0, 9.5), (9.2, 9.8)]
+    B = len(margins)
+    rng = np.random.default_rng(11)
+    t = rng.integers(0, V, 2 * B * T)
+    t[[1, 6, 13, 22]] = -100
+    W = np.zeros((V, H))
+    W[:, :V] = np.eye(V)
+    h = np.zeros((2 * B * T, H))
+    m_seq = [a for a, _ in margins] + [b for _, b in margins]
+    for r in range(2 * B * T):
+        if t[r] >= 0:
+            h[r, t[r]] = m_seq[r // T]
+    loss, gh, _, seq = impl(h, W, t, B, T, beta)
+    counted = t >= 0
+    n = counted.reshape(2 * B, T).sum(axis=1)
+    M = int(counted[: B * T].sum())
+    sig = lambda x: 1.0 / (1.0 + math.exp(-x))
+    q = lambda m: (V - 1) * math.exp(-m) / (1.0 + (V - 1) * math.exp(-m))
+    exp_loss = sum(n[b] * math.log1p((V - 1) * math.exp(-a)) for b, (a, _) in enumerate(margins))
+    exp_loss = exp_loss / M + beta / B * sum(math.log1p(math.exp(bb - a)) for a, bb in margins)
+    assert abs(loss - exp_loss) <= 1e-12 * exp_loss, (loss, exp_loss)
+    exp_seq = np.array([-math.log1p((V - 1) * math.exp(-m)) for m in m_seq])
+    assert np.allclose(seq, exp_seq, rtol=1e-12, atol=0.0), (seq, exp_seq)
+    exp_gh = np.zeros_like(h)
+    for r in range(2 * B * T):
+        if not counted[r]:
+            continue
+        s = r // T
+        a, bb = margins[s % B]
+        if s < B:
+            gt = -q(a) / M - beta / B * sig(bb - a) / n[s]
+        else:
+            gt = beta / B * sig(bb - a) / n[s]
+        exp_gh[r, :V] = -gt / (V - 1)
+        exp_gh[r, t[r]] = gt
+    assert np.allclose(gh, exp_gh, rtol=1e-9, atol=0.0), float(np.max(np.abs(gh - exp_gh)))
 
 
 PINS = [pin_torch, pin_finite_differences, pin_w_zero, pin_beta_zero_is_head_on_chosen,
-        pin_ignored_rows, pin_swap_halves, pin_certain_sequence]
+        pin_ignored_rows, pin_swap_halves, pin_two_valued]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -231,14 +264,22 @@ def _variant(mistake):
         lse = (m + np.log(np.exp(Z - m).sum(axis=1, keepdims=True)))[:, 0]
         P = np.exp(Z - lse[:, None])
         counted = t >= 0 if mistake != "count_ignored" else np.ones(len(t), bool)
+        ar = np.arange(len(t))
         tc = np.where(t >= 0, t, 0)
-        logp = np.where(counted, Z[np.arange(len(t)), tc] - lse, 0.0)
+        zt = Z[ar, tc]
+        if mistake == "cancelling_logp":  # lse - Z_t for every row
+            lp_all = zt - lse
+        else:  # the other classes' mass when the target is the largest logit
+            D = Z - zt[:, None]
+            D[ar, tc] = -np.inf
+            top = D.max(axis=1) <= 0.0
+            lp_all = np.where(top, -np.log1p(np.where(top, np.exp(D).sum(axis=1), 0.0)),
+                              zt - lse)
+        logp = np.where(counted, lp_all, 0.0)
         cnt = counted.reshape(2 * B, T).sum(axis=1).astype(np.float64)
         norm = cnt if mistake != "sum_not_mean" else np.ones(2 * B)
         l_seq = logp.reshape(2 * B, T).sum(axis=1) / norm
-        floor = l_seq > FLOOR if mistake != "no_floor" else np.zeros(2 * B, bool)
-        l_seq = np.where(floor, FLOOR, l_seq)
-        lo = l_seq - np.log1p(-np.exp(l_seq)) if mistake != "odds_is_prob" else l_seq
+        lo = l_seq - np.log(-np.expm1(l_seq)) if mistake != "odds_is_prob" else l_seq
         ratio = lo[:B] - lo[B:]
         red = np.mean if mistake != "or_sum" else np.sum
         l_or = float(red(np.logaddexp(0.0, -ratio)))
@@ -247,15 +288,17 @@ def _variant(mistake):
         loss = float(-logp[sft_rows].sum() / M) + beta * l_or
         sig = 1.0 / (1.0 + np.exp(ratio))
         rej = -sig if mistake != "rejected_sign" else sig
-        dlo = 1.0 / (1.0 - np.exp(l_seq)) if mistake != "odds_is_prob" else np.ones(2 * B)
+        dlo = -1.0 / np.expm1(l_seq) if mistake != "odds_is_prob" else np.ones(2 * B)
         scale = 1.0 / B if mistake != "or_sum" else 1.0
         per_seq = beta * scale * np.concatenate([sig, rej]) * dlo / norm
-        per_seq = np.where(floor, 0.0, per_seq)
         c = np.repeat(per_seq, T)
         c[sft_rows] += 1.0 / M
         c = np.where(counted, c, 0.0)
         G = P.copy()
-        G[np.arange(len(t)), tc] -= np.where(counted, 1.0, 0.0)
+        if mistake == "cancelling_logp":
+            G[ar, tc] -= np.where(counted, 1.0, 0.0)
+        else:
+            G[ar, tc] = np.where(counted, np.expm1(lp_all), G[ar, tc])
         G *= c[:, None]
         return loss, G @ W, G.T @ h, l_seq
 
@@ -268,7 +311,7 @@ def _variant(mistake):
 
 
 MUTANTS = ["sum_not_mean", "odds_is_prob", "or_sum", "sft_both", "rejected_sign",
-           "count_ignored", "no_floor"]
+           "count_ignored", "cancelling_logp"]
 
 
 def test_variant_without_mistake_passes_every_pin():
