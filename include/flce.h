@@ -64,22 +64,24 @@ typedef enum flce_status {
 } flce_status;
 
 /*
- * Bytes of device workspace flce_fwd_bwd needs, with C = min(chunk, N):
- *   bf16 inputs, H % 64 == 0, V % 8 == 0:
+ * Bytes of device workspace flce_fwd_bwd needs, with C = min(chunk, N);
+ * never more than C * V * 4 (the fp32 logits of one chunk; the logits of
+ * all N tokens would take N * V * 4):
+ *   bf16 inputs, H % 64 == 0, V % 8 == 0, H and V below 2^22:
  *        C * V * 2 + C * ceil(V / 128) * 8   (the logits of one token chunk
  *        kept as bf16 exponentials, plus two floats per row and 128-column
  *        slice; each region rounded up to 256 bytes)
  *        + P * H * 4 when chunks are short: if a chunk of r rows gives the
  *        H x r grad_h product <= 128 tiles of 256 x 256 (and V % 64 == 0,
  *        V >= 1024 per part), its K = V contraction is split into s = 2
- *        (<= 128 tiles) or 4 (<= 64) fp32 parts, and P is the larger of
+ *        (<= 128 tiles) or 4 (<= 64) fp32 parts, s halved until the parts
+ *        fit in what remains of C * V * 4 bytes, and P is the larger of
  *        s * r over r = C and r = N mod C
+ *        (when the two regions alone would exceed C * V * 4, a handful of
+ *        rows of a tiny vocabulary, the second form is used)
  *   otherwise:
  *        C * V * 4                           (the fp32 logits of one chunk)
- * (FLCE_GEMM_GENERIC=1 in the environment, which switches the direct-to-LDS
- * GEMM off for comparisons, selects the second form.)
- * Either is at most C * V * 4; the logits of all N tokens would take
- * N * V * 4.  Returns 0 when a size is < 1.  Pure host function.
+ * Returns 0 when a size is < 1.  Pure host function.
  */
 size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t chunk,
                             flce_dtype dt);
@@ -286,7 +288,8 @@ flce_status flce_fwd_bwd_vocab(const void* h, const void* W, const int32_t* targ
  * V), each region rounded up to 256 bytes:
  *   N * Vc * 2            bf16 logits of one vocabulary chunk
  * + N * ceil(V/128) * 8   (max, sum) per row and 128-column slice
- * + N * 12                per-row log-sum-exp, target logit and loss
+ * + N * 16                per-row log-sum-exp, p_t - 1, loss and the
+ *                         mass of the target's 128-column slice
  * + N * H * 4             fp32 grad_h accumulator
  * Returns 0 when a size is < 1 or the shape is not supported by this entry
  * point.  Pure host function.
@@ -308,10 +311,14 @@ size_t flce_vocab_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t vchun
  *              = (b, pairs + b)
  *   counted    a row counts when its target is >= 0; a negative target
  *              marks a prompt or padding row (no loss, zero gradient row)
- *   l_s        mean of log softmax(h_r W^T)[t_r] over the counted rows of s,
- *              at most -2^-14 (a floor: ln(1 - exp(l)) diverges as l -> 0 and
- *              fp32 log-probabilities cannot resolve l above it; at the floor
- *              the sequence gets no odds-ratio gradient)
+ *   l_s        mean of log softmax(h_r W^T)[t_r] over the counted rows of s
+ *              (each log p formed as -ln(1 + S), S the other classes' mass
+ *              relative to the target's from the fp32 logits, so 1 - exp(l)
+ *              keeps its relative precision for a confident model; a
+ *              sequence whose every token has S below fp32's range, logit
+ *              margins beyond about 100, counts as certain: l = 0, which
+ *              leaves finite terms for a chosen sequence and an infinite
+ *              loss for a rejected one, the objective's own limits)
  *   loss       -(1/M) sum over counted chosen rows of log p
  *              + beta * (1/pairs) sum_b ln(1 + exp(-(lo_b - lo_{pairs+b})))
  *              with lo_s = l_s - ln(1 - exp(l_s)) and M the counted chosen
@@ -322,7 +329,7 @@ size_t flce_vocab_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t vchun
  * pair's two sequences in the same chunk; the logits of one chunk are the
  * only [rows, V] array.  A sequence with no counted row, or a target >= V,
  * makes the loss NaN (targets are never read on the host).
- * Supported: FLCE_BF16 with H % 64 == 0, V % 8 == 0 and H below 2^22;
+ * Supported: FLCE_BF16 with H % 64 == 0, V % 8 == 0 and H and V below 2^22;
  * otherwise FLCE_ERR_UNSUPPORTED.  FLCE_ERR_INVALID_ARG for a null required
  * pointer, pairs, seq_len or chunk_pairs < 1, more than 2^31 - 1 rows, a
  * chunk of logits or hidden rows beyond 2^56 elements, or a beta that is not
@@ -342,7 +349,8 @@ flce_status flce_orpo_fwd_bwd(const void* h, const void* W, const int32_t* targe
  *   R * V * 2             bf16 logits of one chunk
  * + R * ceil(V/128) * 8   (max, sum) per row and 128-column slice
  * + K-split rows * H * 4  fp32 grad_h parts when a chunk has few H x R tiles
- * + R * 16                per-row log-sum-exp, target logit, loss and scale
+ * + R * 20                per-row log-sum-exp, p_t - 1, loss, scale and the
+ *                         mass of the target's 128-column slice
  * + 2 * R * H * 2         the chunk's h rows and grad_h rows
  * + R * 4                 the chunk's targets
  * + pairs * 8             per-pair loss terms

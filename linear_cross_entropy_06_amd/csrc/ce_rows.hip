@@ -21,19 +21,34 @@
 //
 // ce_rows_exp (from the logits kernel's exponentiated output: bf16
 // u = 2^(y - mx_q) with y = z log2 e, and one (mx_q, s_q = sum of u) pair
-// per 128-column half tile q of the row)
-//   lse2_i  = log2 sum_q s_q 2^(mx_q), by the same online reduction over the
-//             pairs
-//   z[i, t] = h_i . W_t, recomputed (bf16 rows, fp32 accumulation)
+// per 128-column half tile q of the row, both from the kernel's fp32
+// accumulators)
+//   y_t     = log2(e) h_i . W_t, recomputed (bf16 rows, fp32 accumulation)
+//   S       = sum over j != t of 2^(y_j - y_t): the probability mass of
+//             every other class relative to the target's, a sum of positive
+//             terms, from the pairs of the other half tiles and, for the
+//             target's own half tile q_t, from its stored u values without
+//             the target's (2^(mx_{q_t} - y_t) sum over j in q_t, j != t of
+//             u_j)
+//   loss_i  = ln(1 + S) = -log p_t (log1p: every digit kept as p_t -> 1)
+//   lse2_i  = y_t + log2(1 + S)
 //   G[i, j] = u * 2^(mx_q - lse2_i) * scale, written over u element by
 //             element (same place, same size), then G[i, t] is rewritten as
-//             (2^(z[i,t] log2 e - lse2_i) - 1) * scale.
+//             (p_t - 1) * scale = -S / (1 + S) * scale.
+// Writing log p_t through S rather than as lse - z_t keeps its relative
+// precision when the model is confident (the odds-ratio loss divides by
+// 1 - p).  y_t enters S only as a factor, so the rounding difference
+// between the recomputed and the GEMM's target logit shifts S relatively
+// (by about |y| 2^-24), never absolutely; the target's half tile adds the
+// bf16 rounding of its other u values (at most 2^-9 relatively, on that
+// half tile's share of S only).
 //
 // The exponentials run in base 2 on the hardware v_exp_f32 / v_log_f32.
 //
-// ce_stats_exp / ce_rewrite_exp (vocabulary chunks): the same two halves
-// split in time, for a path that walks the vocabulary in column chunks:
-// after every chunk's pairs exist, lse2_i, log2 z[i, t_i] and the row loss;
+// ce_target_mass / ce_stats_exp / ce_rewrite_exp (vocabulary chunks,
+// preference loss): the same steps split in time.  After each chunk's
+// logits, the target's half-tile mass of the rows whose target falls in the
+// chunk; after every chunk's pairs exist, lse2_i, p_t - 1 and the row loss;
 // then, chunk by chunk, G over that chunk's columns, with the target's
 // element rewritten when it falls in the chunk.
 //
@@ -214,17 +229,62 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// lse2 of a row from its nq (max, sum) pairs (one wave; every lane gets it).
-__device__ __forceinline__ float lse2_from_pairs(const float* pr, int nq, int lane) {
-  float m = -INFINITY, s = 0.0f;
-  for (int q = lane; q < nq; q += 64) combine(m, s, pr[2 * q], pr[2 * q + 1]);
+// (max, sum) over a row's nq pairs except half tile q_skip (one wave;
+// every lane gets it).
+__device__ __forceinline__ void combine_pairs(const float* pr, int nq, int q_skip, int lane,
+                                              float& m, float& a) {
+  m = -INFINITY;
+  a = 0.0f;
+  for (int q = lane; q < nq; q += 64)
+    if (q != q_skip) combine(m, a, pr[2 * q], pr[2 * q + 1]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float m2 = __shfl_xor(m, off, 64);
-    const float s2 = __shfl_xor(s, off, 64);
-    combine(m, s, m2, s2);
+    const float a2 = __shfl_xor(a, off, 64);
+    combine(m, a, m2, a2);
   }
-  return m + log2_hw(s);
+}
+
+// Sum of u over the elements [j0, j1) of a row (j0 even, j1 - j0 <= 128),
+// without element t; two elements per lane, every lane gets the sum.
+__device__ __forceinline__ float half_tile_mass(const uint16_t* ur, int j0, int j1, int t,
+                                                int lane) {
+  const int j = j0 + 2 * lane;
+  float x = 0.0f;
+  if (j < j1) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(ur + j);
+    x = (j != t ? bf16_lo(w) : 0.0f) + (j + 1 < j1 && j + 1 != t ? bf16_hi(w) : 0.0f);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Statistics of a row with a valid target t: from the pairs of every half
+// tile but the target's, that half tile's (max, mass without the target)
+// (mxt, rt), and the target's base-2 logit yt: lse2, the row loss
+// ln(1 + S) and pt1 = p_t - 1 = -S / (1 + S).
+struct RowStats {
+  float lse2, loss, pt1;
+};
+__device__ __forceinline__ RowStats row_stats(const float* pr, int nq, int qt, float rt, float yt,
+                                              int lane) {
+  float m, a;
+  combine_pairs(pr, nq, qt, lane, m, a);
+  combine(m, a, pr[2 * qt], rt);  // (m, a): max and mass of every class but t
+  const float d = m - yt;
+  RowStats r;
+  if (d <= 64.0f) {
+    const float S = a * exp2_hw(d);
+    r.loss = log1pf(S);
+    r.pt1 = -S / (1.0f + S);
+  } else {
+    // another class exceeds the target by 2^64: S > 2^64, p_t = 0 in fp32
+    r.loss = (d + log2_hw(a + exp2_hw(-d))) * kLn2;
+    r.pt1 = -1.0f;
+  }
+  r.lse2 = yt + r.loss * kLog2e;
+  return r;
 }
 
 // Target logit z_t = h_row . W_t (bf16 rows, fp32 accumulation; every lane
@@ -288,64 +348,95 @@ ce_rows_exp_kernel(uint16_t* __restrict__ u, int64_t ldu, const float* __restric
   if (row >= rows) return;
   const int t = targets[row];
   const bool t_ok = (t >= 0) && (t < V);
-
-  // lse2 from the (max, sum) pairs of the row's half tiles.
+  const int nq = (V + kHalfTile - 1) / kHalfTile;
   const float* pr = row_part + (int64_t)row * ldp;
-  const float lse2 = lse2_from_pairs(pr, (V + kHalfTile - 1) / kHalfTile, lane);
-
-  // Target logit (an out-of-range target is never dereferenced: the loss
-  // becomes NaN).
-  const float zt =
-      t_ok ? target_logit(h + (int64_t)row * H, W + (int64_t)t * H, H, lane) : __builtin_nanf("");
-  if (lane == 0) row_loss[(int64_t)row * loss_stride] = (lse2 - to_log2(zt)) * kLn2;
-
-  // G = u * 2^(mx_q - lse2) * scale, in place.
   uint16_t* ur = u + (int64_t)row * ldu;
-  rescale_row<UNROLL>(ur, pr, V, lse2 - log2_hw(scale), lane);
+
+  // An out-of-range target is never dereferenced: the loss becomes NaN.
+  RowStats st;
+  if (t_ok) {
+    const int qt = t / kHalfTile;
+    const float rt = half_tile_mass(ur, kHalfTile * qt, min(kHalfTile * (qt + 1), V), t, lane);
+    const float yt = to_log2(target_logit(h + (int64_t)row * H, W + (int64_t)t * H, H, lane));
+    st = row_stats(pr, nq, qt, rt, yt, lane);
+  } else {
+    float m, a;
+    combine_pairs(pr, nq, -1, lane, m, a);
+    st = RowStats{m + log2_hw(a), __builtin_nanf(""), 0.0f};
+  }
+  if (lane == 0) row_loss[(int64_t)row * loss_stride] = st.loss;
+
+  // G = u * 2^(mx_q - lse2) * scale, in place (after every lane's read of
+  // the target's half tile above: the shuffles order them).
+  rescale_row<UNROLL>(ur, pr, V, st.lse2 - log2_hw(scale), lane);
   if (t_ok && lane == 0) {
     // After this wave's stores of the row have completed (the target's
     // element among them), overwrite that element.
     __builtin_amdgcn_s_waitcnt(0);
-    const float pt = exp2_hw(to_log2(zt) - lse2);
-    ur[t] = (uint16_t)bf16_bits((pt - 1.0f) * scale);
+    ur[t] = (uint16_t)bf16_bits(st.pt1 * scale);
   }
 }
 
-// Vocabulary-chunked statistics: after the exponentiated logits of every
-// vocabulary chunk have left their (max, sum) pairs, per row lse2 (all V
-// columns), log2 of the target logit, and the row loss.
+// Vocabulary chunk [v0, v0 + n) of rows' exponentiated logits (row pitch
+// ldu, chunk-local columns; v0 % 128 == 0): for each row whose target falls
+// in the chunk, the mass of its half tile without the target, into rt[row].
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
-ce_stats_exp_kernel(const float* __restrict__ row_part, int64_t ldp,
+ce_target_mass_kernel(const uint16_t* __restrict__ u, int64_t ldu,
+                      const int32_t* __restrict__ targets, int rows, int v0, int n,
+                      float* __restrict__ rt) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int t = targets[row] - v0;
+  if (t < 0 || t >= n) return;
+  const int qt = t / kHalfTile;
+  const float m = half_tile_mass(u + (int64_t)row * ldu, kHalfTile * qt,
+                                 min(kHalfTile * (qt + 1), n), t, lane);
+  if (lane == 0) rt[row] = m;
+}
+
+// Statistics only: after the exponentiated logits of every vocabulary chunk
+// have left their (max, sum) pairs and the target's half-tile mass rt, per
+// row lse2 (all V columns), p_t - 1 and the row loss.
+__global__ void __launch_bounds__(64 * kWavesPerBlock)
+ce_stats_exp_kernel(const float* __restrict__ row_part, int64_t ldp, const float* __restrict__ rt,
                     const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int H,
                     const int32_t* __restrict__ targets, int rows, int V,
-                    float* __restrict__ lse2_out, float* __restrict__ zt2_out,
+                    float* __restrict__ lse2_out, float* __restrict__ pt1_out,
                     float* __restrict__ row_loss) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int t = targets[row];
   const bool t_ok = (t >= 0) && (t < V);
-  const float lse2 =
-      lse2_from_pairs(row_part + (int64_t)row * ldp, (V + kHalfTile - 1) / kHalfTile, lane);
-  const float zt =
-      t_ok ? target_logit(h + (int64_t)row * H, W + (int64_t)t * H, H, lane) : __builtin_nanf("");
+  const int nq = (V + kHalfTile - 1) / kHalfTile;
+  const float* pr = row_part + (int64_t)row * ldp;
+  RowStats st;
+  if (t_ok) {
+    const float yt = to_log2(target_logit(h + (int64_t)row * H, W + (int64_t)t * H, H, lane));
+    st = row_stats(pr, nq, t / kHalfTile, rt[row], yt, lane);
+  } else {
+    float m, a;
+    combine_pairs(pr, nq, -1, lane, m, a);
+    st = RowStats{m + log2_hw(a), __builtin_nanf(""), 0.0f};
+  }
   if (lane == 0) {
-    lse2_out[row] = lse2;
-    zt2_out[row] = to_log2(zt);
-    row_loss[row] = (lse2 - to_log2(zt)) * kLn2;
+    lse2_out[row] = st.lse2;
+    pt1_out[row] = st.pt1;
+    row_loss[row] = st.loss;
   }
 }
 
 // Vocabulary-chunked gradient of one chunk of columns [v0, v0 + n): u -> G
 // in place with the rows' lse2 from every chunk, and the target's element
-// (when it falls in the chunk) rewritten as (2^(zt2 - lse2) - 1) * scale.
-// With row_scale, row i takes the scale row_scale[i] instead (any sign; 0
-// clears the row) and a negative target leaves no one-hot element.
+// (when it falls in the chunk) rewritten as (p_t - 1) * scale.  With
+// row_scale, row i takes the scale row_scale[i] instead (any sign; 0 clears
+// the row) and a negative target leaves no one-hot element.
 template <int UNROLL>
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
 ce_rewrite_exp_kernel(uint16_t* __restrict__ u, int64_t ldu, const float* __restrict__ row_part,
                       int64_t ldp, const float* __restrict__ lse2_in,
-                      const float* __restrict__ zt2_in, const int32_t* __restrict__ targets,
+                      const float* __restrict__ pt1_in, const int32_t* __restrict__ targets,
                       int rows, int v0, int n, float scale, const float* __restrict__ row_scale) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
@@ -363,8 +454,7 @@ ce_rewrite_exp_kernel(uint16_t* __restrict__ u, int64_t ldu, const float* __rest
   const int t = targets[row] - v0;
   if (t >= 0 && t < n && lane == 0) {
     __builtin_amdgcn_s_waitcnt(0);
-    const float pt = exp2_hw(zt2_in[row] - lse2);
-    ur[t] = (uint16_t)bf16_bits((pt - 1.0f) * scale);
+    ur[t] = (uint16_t)bf16_bits(pt1_in[row] * scale);
   }
 }
 
@@ -527,21 +617,32 @@ hipError_t launch_ce_rows_exp(uint16_t* u, int64_t ldu, const float* row_part, i
   return hipGetLastError();
 }
 
-hipError_t launch_ce_stats_exp(const float* row_part, int64_t ldp, const uint16_t* h,
-                               const uint16_t* W, int H, const int32_t* targets, int rows, int V,
-                               float* lse2, float* zt2, float* row_loss, hipStream_t s) {
+hipError_t launch_ce_target_mass(const uint16_t* u, int64_t ldu, const int32_t* targets,
+                                 int rows, int v0, int n, float* rt, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if ((v0 % kHalfTile) || (ldu % 2) || (reinterpret_cast<uintptr_t>(u) & 3) || n < 1)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ce_target_mass_kernel, dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock),
+                     dim3(64 * kWavesPerBlock), 0, s, u, ldu, targets, rows, v0, n, rt);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_stats_exp(const float* row_part, int64_t ldp, const float* rt,
+                               const uint16_t* h, const uint16_t* W, int H,
+                               const int32_t* targets, int rows, int V, float* lse2, float* pt1,
+                               float* row_loss, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if ((H % 8) || (reinterpret_cast<uintptr_t>(h) & 15) || (reinterpret_cast<uintptr_t>(W) & 15) ||
-      ldp < 2 * ((V + kHalfTile - 1) / kHalfTile))
+      !rt || ldp < 2 * ((V + kHalfTile - 1) / kHalfTile))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(ce_stats_exp_kernel, dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock),
-                     dim3(64 * kWavesPerBlock), 0, s, row_part, ldp, h, W, H, targets, rows, V,
-                     lse2, zt2, row_loss);
+                     dim3(64 * kWavesPerBlock), 0, s, row_part, ldp, rt, h, W, H, targets, rows,
+                     V, lse2, pt1, row_loss);
   return hipGetLastError();
 }
 
 hipError_t launch_ce_rewrite_exp(uint16_t* u, int64_t ldu, const float* row_part, int64_t ldp,
-                                 const float* lse2, const float* zt2, const int32_t* targets,
+                                 const float* lse2, const float* pt1, const int32_t* targets,
                                  int rows, int v0, int n, float scale, const float* row_scale,
                                  hipStream_t s) {
   if (rows <= 0) return hipSuccess;
@@ -550,7 +651,7 @@ hipError_t launch_ce_rewrite_exp(uint16_t* u, int64_t ldu, const float* row_part
       ldp < 2 * ((n + kHalfTile - 1) / kHalfTile))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL((ce_rewrite_exp_kernel<4>), dim3((rows + kWavesPerBlock - 1) / kWavesPerBlock),
-                     dim3(64 * kWavesPerBlock), 0, s, u, ldu, row_part, ldp, lse2, zt2, targets,
+                     dim3(64 * kWavesPerBlock), 0, s, u, ldu, row_part, ldp, lse2, pt1, targets,
                      rows, v0, n, scale, row_scale);
   return hipGetLastError();
 }

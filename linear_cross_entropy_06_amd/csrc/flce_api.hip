@@ -46,10 +46,11 @@ inline hipError_t gemm(flce_dtype dt, bool a_kc, bool b_kc, int epi, bool vec,
 
 // The bf16 path whose logits kernel writes exponentiated bf16 logits and
 // their (max, sum) pairs (direct-to-LDS kernel: K = H a multiple of 64,
-// V a multiple of 8).  Every other case keeps fp32 logits.
+// V a multiple of 8, both leading dimensions below 2^22).  Every other case
+// keeps fp32 logits.
 inline bool exp_path(int64_t H, int64_t V, flce_dtype dt) {
   return dt == FLCE_BF16 && V % 8 == 0 && H % 64 == 0 && H < (int64_t{1} << 22) &&
-         flce::gemm_bf16_dma_enabled();
+         V < (int64_t{1} << 22);
 }
 
 // (max, sum) pairs per row on the exponentiated path.
@@ -57,20 +58,23 @@ inline int64_t n_half_tiles(int64_t V) { return (V + flce::kHalfTile - 1) / flce
 
 // K split of the grad_h contraction (H x rows output, K = V) when its
 // 256 x 256 tiles would not fill the chip: 4 parts for <= 64 tiles, 2 for
-// <= 128 (exponentiated path with V % 64 == 0, at least 16 slabs a part).
-inline int grad_h_splits(int64_t H, int64_t rows, int64_t V) {
+// <= 128 (exponentiated path with V % 64 == 0, at least 16 slabs a part),
+// halved until the fp32 parts fit in `room` bytes (1 when none fits).
+inline int grad_h_splits(int64_t H, int64_t rows, int64_t V, int64_t room) {
   const int64_t tiles = ((H + 255) / 256) * ((rows + 255) / 256);
-  const int s = tiles <= 64 ? 4 : tiles <= 128 ? 2 : 1;
-  return (V % 64 == 0 && V / 64 >= 16 * s) ? s : 1;
+  int s = tiles <= 64 ? 4 : tiles <= 128 ? 2 : 1;
+  if (V % 64 != 0 || V / 64 < 16 * s) return 1;
+  while (s > 1 && s * rows * H * 4 > room) s /= 2;
+  return s;
 }
 
 // Rows of the fp32 [rows][H] part buffer the K split needs: the larger of
 // splits(rows) * rows over the chunk sizes that occur (C, and N mod C).
-inline int64_t split_scratch_rows(int64_t N, int64_t H, int64_t C, int64_t V) {
+inline int64_t split_scratch_rows(int64_t N, int64_t H, int64_t C, int64_t V, int64_t room) {
   int64_t best = 0;
   for (int64_t r : {C, N % C}) {
     if (r <= 0) continue;
-    const int s = grad_h_splits(H, r, V);
+    const int s = grad_h_splits(H, r, V, room);
     if (s > 1 && s * r > best) best = s * r;
   }
   return best;
@@ -78,16 +82,26 @@ inline int64_t split_scratch_rows(int64_t N, int64_t H, int64_t C, int64_t V) {
 
 inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-// Byte offsets of the exponentiated path's workspace regions.
+// Byte offsets of the exponentiated path's workspace regions: u [C][V]
+// bf16, the pairs [C][ceil(V/128)][2], then the grad_h K-split parts in
+// whatever remains of C * V * 4 bytes (`room`).
 struct ExpLayout {
-  int64_t pairs, parts, total;
+  int64_t pairs, parts, room, total;
 };
 inline ExpLayout exp_layout(int64_t N, int64_t C, int64_t H, int64_t V) {
   ExpLayout l;
   l.pairs = round_up(C * V * 2, 256);
   l.parts = round_up(l.pairs + C * n_half_tiles(V) * 8, 256);
-  l.total = l.parts + split_scratch_rows(N, H, C, V) * H * 4;
+  l.room = C * V * 4 > l.parts ? C * V * 4 - l.parts : 0;
+  l.total = l.parts + split_scratch_rows(N, H, C, V, l.room) * H * 4;
   return l;
+}
+
+// The token-chunked path runs exponentiated when its layout fits the fp32
+// logits' C * V * 4 bytes (it does unless the chunk is a handful of rows of
+// a tiny vocabulary), so the workspace never exceeds C * V * 4.
+inline bool use_exp(int64_t N, int64_t C, int64_t H, int64_t V, flce_dtype dt) {
+  return exp_path(H, V, dt) && exp_layout(N, C, H, V).parts <= C * V * 4;
 }
 
 }  // namespace
@@ -99,7 +113,7 @@ extern "C" size_t flce_workspace_bytes(int64_t N, int64_t H, int64_t V, int64_t 
   if (!area_ok(C, V) || !area_ok(C, H)) return 0;
   // bf16 logits of one chunk + 2 floats per row and half tile (+ grad_h
   // K-split parts for short chunks)
-  if (exp_path(H, V, dt)) return static_cast<size_t>(exp_layout(N, C, H, V).total);
+  if (use_exp(N, C, H, V, dt)) return static_cast<size_t>(exp_layout(N, C, H, V).total);
   return static_cast<size_t>(C) * static_cast<size_t>(V) * 4u;  // fp32 logits of one chunk
 }
 
@@ -165,7 +179,7 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
   const int64_t es = esize(dt);
   const bool bf16 = dt == FLCE_BF16;
   const bool vec = (V % 8) == 0;
-  const bool expo = exp_path(H, V, dt);
+  const bool expo = use_exp(N, C, H, V, dt);
   const float inv_n = static_cast<float>(1.0 / static_cast<double>(N));
   // Workspace: fp32 logits Z (row pitch V) that become G in place (bf16 G in
   // the first half of each row, fp32 G over the row), or on the
@@ -239,7 +253,7 @@ flce_status fwd_bwd_impl(const void* h, const void* W, const int32_t* targets, i
     flce::GemmArgs g4{W, H, g_base, ldg, ghc, H, static_cast<int>(H), rows, static_cast<int>(V),
                       0};
     g4.group_m = 4;
-    const int splits = expo ? grad_h_splits(H, rows, V) : 1;
+    const int splits = expo ? grad_h_splits(H, rows, V, lay.room) : 1;
     mk.before();
     if (splits > 1) {
       g4.out = parts;
@@ -473,7 +487,7 @@ inline VocabLayout vocab_layout(int64_t N, int64_t H, int64_t V, int64_t Vc) {
   VocabLayout l;
   l.pairs = round_up(N * Vc * 2, 256);                         // u [N][Vc] bf16
   l.stats = round_up(l.pairs + N * n_half_tiles(V) * 8, 256);  // pairs [N][2 ceil(V/128)]
-  l.acc = round_up(l.stats + 3 * N * 4, 256);                  // lse2, zt2, row loss [N]
+  l.acc = round_up(l.stats + 4 * N * 4, 256);                  // lse2, pt1, loss, rt [N]
   l.total = l.acc + N * H * 4;                                 // grad_h accumulator fp32
   return l;
 }
@@ -483,8 +497,7 @@ inline VocabLayout vocab_layout(int64_t N, int64_t H, int64_t V, int64_t Vc) {
 // 128-column half tiles.
 inline bool vocab_path_ok(int64_t H, int64_t V, int64_t vchunk, flce_dtype dt) {
   return dt == FLCE_BF16 && H % 64 == 0 && H < (int64_t{1} << 22) && V % 64 == 0 &&
-         V < (int64_t{1} << 22) && (vchunk >= V || vchunk % flce::kHalfTile == 0) &&
-         flce::gemm_bf16_dma_enabled();
+         V < (int64_t{1} << 22) && (vchunk >= V || vchunk % flce::kHalfTile == 0);
 }
 
 }  // namespace
@@ -522,8 +535,9 @@ extern "C" flce_status flce_fwd_bwd_vocab(const void* h, const void* W, const in
   uint16_t* u = reinterpret_cast<uint16_t*>(ws);
   float* pairs = reinterpret_cast<float*>(ws + lay.pairs);
   float* lse2 = reinterpret_cast<float*>(ws + lay.stats);
-  float* zt2 = lse2 + N;
-  float* row_loss = zt2 + N;
+  float* pt1 = lse2 + N;
+  float* row_loss = pt1 + N;
+  float* rt = row_loss + N;
   float* gacc = reinterpret_cast<float*>(ws + lay.acc);
   const int64_t ldp = 2 * n_half_tiles(V);
   const int rows = static_cast<int>(N);
@@ -542,11 +556,17 @@ extern "C" flce_status flce_fwd_bwd_vocab(const void* h, const void* W, const in
     return flce::launch_gemm_bf16(true, true, flce::kExpBF16, true, g, stream);
   };
 
-  // Pass 1: statistics.
-  for (int64_t v0 = 0; v0 < V; v0 += Vc)
-    if (logits(v0, (V - v0) < Vc ? (V - v0) : Vc) != hipSuccess) return FLCE_ERR_HIP;
-  if (flce::launch_ce_stats_exp(pairs, ldp, h16, W16, static_cast<int>(H), targets, rows,
-                                static_cast<int>(V), lse2, zt2, row_loss, stream) != hipSuccess ||
+  // Pass 1: statistics (the target's half-tile mass taken from the chunk
+  // that holds the target, while its u values are in the workspace).
+  for (int64_t v0 = 0; v0 < V; v0 += Vc) {
+    const int64_t n = (V - v0) < Vc ? (V - v0) : Vc;
+    if (logits(v0, n) != hipSuccess ||
+        flce::launch_ce_target_mass(u, Vc, targets, rows, static_cast<int>(v0),
+                                    static_cast<int>(n), rt, stream) != hipSuccess)
+      return FLCE_ERR_HIP;
+  }
+  if (flce::launch_ce_stats_exp(pairs, ldp, rt, h16, W16, static_cast<int>(H), targets, rows,
+                                static_cast<int>(V), lse2, pt1, row_loss, stream) != hipSuccess ||
       flce::launch_loss_sum(row_loss, 1, rows, inv_n, 1, loss, stream) != hipSuccess)
     return FLCE_ERR_HIP;
 
@@ -554,7 +574,7 @@ extern "C" flce_status flce_fwd_bwd_vocab(const void* h, const void* W, const in
   for (int64_t v0 = 0; v0 < V; v0 += Vc) {
     const int64_t n = (V - v0) < Vc ? (V - v0) : Vc;
     if (logits(v0, n) != hipSuccess) return FLCE_ERR_HIP;
-    if (flce::launch_ce_rewrite_exp(u, Vc, pairs + 2 * (v0 / flce::kHalfTile), ldp, lse2, zt2,
+    if (flce::launch_ce_rewrite_exp(u, Vc, pairs + 2 * (v0 / flce::kHalfTile), ldp, lse2, pt1,
                                     targets, rows, static_cast<int>(v0), static_cast<int>(n),
                                     inv_n, nullptr, stream) != hipSuccess)
       return FLCE_ERR_HIP;
@@ -606,20 +626,23 @@ namespace {
 struct OrpoLayout {
   int64_t pairs, parts, stats, hc, ghc, tc, stage, count, total;
 };
+// The preference loss sizes its K-split parts without a cap (its workspace
+// also stages the chunk's hidden rows and gradients).
+constexpr int64_t kOrpoSplitRoom = int64_t{1} << 62;
 inline OrpoLayout orpo_layout(int64_t B, int64_t T, int64_t Pc, int64_t H, int64_t V) {
   const int64_t R = 2 * Pc * T;        // rows of a full chunk
   const int64_t Rl = 2 * (B % Pc) * T; // rows of a shorter last chunk (0: none)
   int64_t split_rows = 0;
   for (int64_t r : {R, Rl}) {
     if (r <= 0) continue;
-    const int sp = grad_h_splits(H, r, V);
+    const int sp = grad_h_splits(H, r, V, kOrpoSplitRoom);
     if (sp > 1 && sp * r > split_rows) split_rows = sp * r;
   }
   OrpoLayout l;
   l.pairs = round_up(R * V * 2, 256);                             // u [R][V] bf16
   l.parts = round_up(l.pairs + R * n_half_tiles(V) * 8, 256);     // (max, sum) pairs
   l.stats = round_up(l.parts + split_rows * H * 4, 256);          // grad_h K-split parts
-  l.hc = round_up(l.stats + 4 * R * 4, 256);                      // lse2, zt2, loss, coef
+  l.hc = round_up(l.stats + 5 * R * 4, 256);                      // lse2, pt1, loss, coef, rt
   l.ghc = round_up(l.hc + R * H * 2, 256);                        // h_c [R][H] bf16
   l.tc = round_up(l.ghc + R * H * 2, 256);                        // grad_h_c [R][H] bf16
   l.stage = round_up(l.tc + R * 4, 256);                          // t_c [R]
@@ -674,9 +697,10 @@ extern "C" flce_status flce_orpo_fwd_bwd(const void* h, const void* W, const int
   float* parts = reinterpret_cast<float*>(ws + lay.parts);
   const int64_t R = 2 * Pc * T;
   float* lse2 = reinterpret_cast<float*>(ws + lay.stats);
-  float* zt2 = lse2 + R;
-  float* row_loss = zt2 + R;
+  float* pt1 = lse2 + R;
+  float* row_loss = pt1 + R;
   float* coef = row_loss + R;
+  float* rt = coef + R;
   uint16_t* hc = reinterpret_cast<uint16_t*>(ws + lay.hc);
   uint16_t* ghc = reinterpret_cast<uint16_t*>(ws + lay.ghc);
   int32_t* tc = reinterpret_cast<int32_t*>(ws + lay.tc);
@@ -714,13 +738,15 @@ extern "C" flce_status flce_orpo_fwd_bwd(const void* h, const void* W, const int
       return FLCE_ERR_HIP;
 
     // 3.-5. row statistics, per-pair terms and row scales, G in place.
-    if (flce::launch_ce_stats_exp(rpairs, ldp, hc, W16, static_cast<int>(H), tc, rows,
-                                  static_cast<int>(V), lse2, zt2, row_loss, stream) !=
+    if (flce::launch_ce_target_mass(u, V, tc, rows, 0, static_cast<int>(V), rt, stream) !=
             hipSuccess ||
-        flce::launch_orpo_coef(lse2, zt2, tc, static_cast<int>(pc), static_cast<int>(T),
+        flce::launch_ce_stats_exp(rpairs, ldp, rt, hc, W16, static_cast<int>(H), tc, rows,
+                                  static_cast<int>(V), lse2, pt1, row_loss, stream) !=
+            hipSuccess ||
+        flce::launch_orpo_coef(row_loss, tc, static_cast<int>(pc), static_cast<int>(T),
                                static_cast<int>(B), static_cast<int>(p0), beta, count, coef,
                                seq_logp, stage, stream) != hipSuccess ||
-        flce::launch_ce_rewrite_exp(u, V, rpairs, ldp, lse2, zt2, tc, rows, 0,
+        flce::launch_ce_rewrite_exp(u, V, rpairs, ldp, lse2, pt1, tc, rows, 0,
                                     static_cast<int>(V), 1.0f, coef, stream) != hipSuccess)
       return FLCE_ERR_HIP;
 
@@ -728,7 +754,7 @@ extern "C" flce_status flce_orpo_fwd_bwd(const void* h, const void* W, const int
     //    to the chunk's rows of grad_h.
     flce::GemmArgs g4{W, H, u, V, ghc, H, static_cast<int>(H), rows, static_cast<int>(V), 0};
     g4.group_m = 4;
-    const int splits = grad_h_splits(H, rows, V);
+    const int splits = grad_h_splits(H, rows, V, kOrpoSplitRoom);
     hipError_t e;
     if (splits > 1) {
       g4.out = parts;

@@ -74,9 +74,6 @@ bool gemm_bf16_dma_supported(bool a_kc, bool b_kc, const GemmArgs& g);
 // True when launch_gemm_bf16 with these arguments runs the direct-to-LDS
 // kernel (the only one with the kExpBF16 epilogue).
 bool gemm_bf16_uses_dma(bool a_kc, bool b_kc, bool vec, const GemmArgs& g);
-// Whether the direct-to-LDS kernel may be used at all in this process (it
-// can be switched off for comparisons, see gemm_bf16.hip).
-bool gemm_bf16_dma_enabled();
 hipError_t launch_gemm_bf16_dma(bool a_kc, bool b_kc, int epi, const GemmArgs& g,
                                 hipStream_t s);
 
@@ -99,24 +96,39 @@ hipError_t launch_ce_rows_bf16(uint16_t* z, int64_t ldz, const int32_t* targets,
 // The same from exponentiated logits (kExpBF16 output u at pitch ldu, with
 // its (max, sum) pairs): u is rewritten in place as the bf16 gradient.  The
 // target logit of row i is recomputed as the dot product of h[i] and
-// W[targets[i]] (bf16 rows of H elements, fp32 accumulation).
+// W[targets[i]] (bf16 rows of H elements, fp32 accumulation); the row loss
+// is ln(1 + S) with S = sum over j != t of exp(z_j - z_t), formed from the
+// other half tiles' pairs and the target's half tile's u values without the
+// target (positive terms only), and G[i, t] = -S / (1 + S) * scale.
 hipError_t launch_ce_rows_exp(uint16_t* u, int64_t ldu, const float* row_part, int64_t ldp,
                               const uint16_t* h, const uint16_t* W, int H,
                               const int32_t* targets, int rows, int V, float scale,
                               float* row_loss, int64_t loss_stride, hipStream_t s);
 
-// Vocabulary-chunked path, statistics: per row, lse2 over all V columns
-// from the pairs (row pitch ldp floats, 2 * ceil(V / 128) used), zt2 =
-// log2(e) * h_i . W_{t_i}, and row_loss = (lse2 - zt2) ln 2; [rows] each.
-hipError_t launch_ce_stats_exp(const float* row_part, int64_t ldp, const uint16_t* h,
-                               const uint16_t* W, int H, const int32_t* targets, int rows, int V,
-                               float* lse2, float* zt2, float* row_loss, hipStream_t s);
+// Split form of the same (vocabulary chunks, preference loss).
+//   ce_target_mass: for a chunk [v0, v0 + n) of columns (v0 % 128 == 0; u
+//     rows at pitch ldu hold the chunk's columns from 0), every row whose
+//     target falls in the chunk gets rt[row] = the sum of u over its
+//     target's half tile without the target.
+//   ce_stats_exp: once every chunk's pairs (row pitch ldp floats,
+//     2 * ceil(V / 128) used) and rt exist: per row lse2 over all V columns,
+//     pt1 = p_t - 1 and row_loss = ln(1 + S) = -log p_t, [rows] each.  A
+//     row whose target is outside [0, V) gets the log-sum-exp of all
+//     columns, pt1 = 0 and a NaN loss.
+hipError_t launch_ce_target_mass(const uint16_t* u, int64_t ldu, const int32_t* targets,
+                                 int rows, int v0, int n, float* rt, hipStream_t s);
+hipError_t launch_ce_stats_exp(const float* row_part, int64_t ldp, const float* rt,
+                               const uint16_t* h, const uint16_t* W, int H,
+                               const int32_t* targets, int rows, int V, float* lse2, float* pt1,
+                               float* row_loss, hipStream_t s);
 // Vocabulary-chunked path, gradient of columns [v0, v0 + n) (v0 % 128 == 0,
 // n % 8 == 0): u (row pitch ldu) -> (u 2^(mx_q - lse2) - [j == t]) * scale
-// in place; row_part points at the chunk's first pair of row 0.  A non-null
-// row_scale gives each row its own scale (any sign) in place of `scale`.
+// in place, the target's element (when it falls in the chunk) being
+// pt1 * scale; row_part points at the chunk's first pair of row 0.  A
+// non-null row_scale gives each row its own scale (any sign) in place of
+// `scale`.
 hipError_t launch_ce_rewrite_exp(uint16_t* u, int64_t ldu, const float* row_part, int64_t ldp,
-                                 const float* lse2, const float* zt2, const int32_t* targets,
+                                 const float* lse2, const float* pt1, const int32_t* targets,
                                  int rows, int v0, int n, float scale, const float* row_scale,
                                  hipStream_t s);
 
@@ -125,8 +137,8 @@ hipError_t launch_ce_rewrite_exp(uint16_t* u, int64_t ldu, const float* row_part
 // marks a row that does not count.
 //   orpo_count: *count = number of rows r < n with targets[r] >= 0.
 //   orpo_coef:  for the Pc pairs [p0, p0 + Pc) staged as one chunk (chosen
-//     rows [0, Pc T), rejected rows [Pc T, 2 Pc T), with lse2 / zt2 of each
-//     row from launch_ce_stats_exp): each row's gradient scale
+//     rows [0, Pc T), rejected rows [Pc T, 2 Pc T), with each row's
+//     -log p_t from launch_ce_stats_exp in row_loss): each row's gradient scale
 //     c = -dloss/dlog p (0 for rows that do not count) into coef, each
 //     sequence's mean log-probability into seq_logp[p] and seq_logp[B + p]
 //     (when non-null), and per pair the chosen rows' -sum log p and the
@@ -134,7 +146,7 @@ hipError_t launch_ce_rewrite_exp(uint16_t* u, int64_t ldu, const float* row_part
 //   orpo_loss:  *loss = sum_p stage[2p] / count + beta / B sum_p stage[2p+1],
 //     fixed-order fp64 sums.
 hipError_t launch_orpo_count(const int32_t* targets, int64_t n, int* count, hipStream_t s);
-hipError_t launch_orpo_coef(const float* lse2, const float* zt2, const int32_t* targets, int Pc,
+hipError_t launch_orpo_coef(const float* row_loss, const int32_t* targets, int Pc,
                             int T, int B, int p0, float beta, const int* count, float* coef,
                             float* seq_logp, float* stage, hipStream_t s);
 hipError_t launch_orpo_loss(const float* stage, int B, float beta, const int* count, float* loss,

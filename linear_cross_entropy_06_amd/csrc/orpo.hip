@@ -6,8 +6,7 @@
 // chunked post-training losses that take the LM-head weight, the hidden
 // states and the targets and return the loss; the objective is the
 // published one of ORPO (Hong, Lee and Thorne, 2024):
-//   l_s      min(mean over the counted rows of sequence s of log p(t_r),
-//            -2^-14)
+//   l_s      = mean over the counted rows of sequence s of log p(t_r)
 //   lo_s     = l_s - ln(1 - exp(l_s))                       (log odds)
 //   L_OR     = (1/B) sum_b ln(1 + exp(-(lo_b - lo_{B+b})))
 //   L_SFT    = -(1/M) sum over counted chosen rows of log p(t_r)
@@ -16,13 +15,17 @@
 //   c_r = [chosen] / M + (+/-) beta / B * sigmoid(-(lo_b - lo_{B+b}))
 //         / ((1 - exp(l_s)) n_s)
 // (+ for the chosen, - for the rejected row of pair b; n_s counted rows of
-// the row's sequence; no odds-ratio part for a sequence at the floor).  The
-// floor keeps ln(1 - exp(l)) finite when a sequence is certain: an fp32
-// log-probability (log-sum-exp minus target logit) is off by about one unit
-// in the last place of the logits, 2^-18 to 2^-16 at magnitudes 30 to 100,
-// so a mean closer to 0 is not resolvable (and may round to >= 0); at the
-// floor the odds-ratio term does not depend on that sequence.  Sums run in fp64 in a fixed order
-// (deterministic).
+// the row's sequence).  With P = exp(l), Q = 1 - P and odds P / Q, the
+// odds-ratio factor is evaluated as
+//   sigmoid(-ratio) / Q_w = 1 / (Q_w + P_w Q_l / P_l)
+//   sigmoid(-ratio) / Q_l = 1 / (Q_l + Q_l^2 P_w / (Q_w P_l))
+// (exp(ratio) = odds_w / odds_l), which equal the chain-rule forms and
+// reach their limits as a sequence becomes certain (Q -> 0): a certain
+// chosen sequence leaves finite terms, a certain rejected one an infinite
+// loss, as the objective itself does.  Each log p(t_r) comes from the row pass as
+// -ln(1 + S_r), S_r the other classes' mass relative to the target's, so
+// l and Q = -expm1(l) keep their relative precision near P = 1.  Sums run
+// in fp64 in a fixed order (deterministic).
 #include "flce_internal.h"
 
 #include <math.h>
@@ -30,8 +33,6 @@
 namespace flce {
 namespace {
 
-constexpr double kLn2d = 0.6931471805599453;
-constexpr double kLogpFloor = -6.103515625e-05;  // -2^-14
 constexpr int kWaves = 4;
 constexpr int kCountThreads = 1024;
 constexpr int kLossThreads = 256;
@@ -64,44 +65,42 @@ __device__ __forceinline__ int wave_sum(int x) {
 
 // One wave per pair q of the chunk.
 __global__ void __launch_bounds__(64 * kWaves)
-orpo_coef_kernel(const float* __restrict__ lse2, const float* __restrict__ zt2,
-                 const int32_t* __restrict__ targets, int Pc, int T, int B, int p0, float beta,
-                 const int* __restrict__ count, float* __restrict__ coef,
-                 float* __restrict__ seq_logp, float* __restrict__ stage) {
+orpo_coef_kernel(const float* __restrict__ row_loss, const int32_t* __restrict__ targets, int Pc,
+                 int T, int B, int p0, float beta, const int* __restrict__ count,
+                 float* __restrict__ coef, float* __restrict__ seq_logp,
+                 float* __restrict__ stage) {
   const int lane = threadIdx.x & 63;
   const int q = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (q >= Pc) return;
   const int64_t rw = (int64_t)q * T;         // chosen rows of the pair
   const int64_t rl = (int64_t)(Pc + q) * T;  // rejected rows
-  double sw = 0.0, sl = 0.0;                 // sums of log2 p over counted rows
+  double sw = 0.0, sl = 0.0;                 // sums of log p over counted rows
   int nw = 0, nl = 0;
   for (int k = lane; k < T; k += 64) {
     if (targets[rw + k] >= 0) {
-      sw += (double)zt2[rw + k] - (double)lse2[rw + k];
+      sw -= (double)row_loss[rw + k];
       ++nw;
     }
     if (targets[rl + k] >= 0) {
-      sl += (double)zt2[rl + k] - (double)lse2[rl + k];
+      sl -= (double)row_loss[rl + k];
       ++nl;
     }
   }
-  sw = wave_sum(sw) * kLn2d;  // natural log from here on
-  sl = wave_sum(sl) * kLn2d;
+  sw = wave_sum(sw);
+  sl = wave_sum(sl);
   nw = wave_sum(nw);
   nl = wave_sum(nl);
-  // Mean log-probabilities (0 / 0 = NaN for a sequence with no counted row;
-  // NaN compares false and stays NaN).
-  double lw = sw / (double)nw, ll = sl / (double)nl;
-  const bool fw = lw > kLogpFloor, fl = ll > kLogpFloor;
-  if (fw) lw = kLogpFloor;
-  if (fl) ll = kLogpFloor;
+  // Mean log-probabilities (0 / 0 = NaN for a sequence with no counted row).
+  const double lw = sw / (double)nw, ll = sl / (double)nl;
+  const double pw = exp(lw), pl = exp(ll);
   const double qw = -expm1(lw), ql = -expm1(ll);  // 1 - P, accurate near P = 1
   const double ratio = (lw - log(qw)) - (ll - log(ql));
   const double or_term = ratio > 0.0 ? log1p(exp(-ratio)) : -ratio + log1p(exp(ratio));
-  const double sig_neg = 1.0 / (1.0 + exp(ratio));
-  const double k_or = (double)beta / (double)B * sig_neg;
-  const float cw = (float)(1.0 / (double)count[0] + (fw ? 0.0 : k_or / (qw * (double)nw)));
-  const float cl = fl ? 0.0f : (float)(-k_or / (ql * (double)nl));
+  const double k_or = (double)beta / (double)B;
+  const double cw_or = k_or / ((double)nw * (qw + pw * ql / pl));
+  const double cl_or = -k_or / ((double)nl * (ql + ql * ql * pw / (qw * pl)));
+  const float cw = (float)(1.0 / (double)count[0] + cw_or);
+  const float cl = (float)cl_or;
   for (int k = lane; k < T; k += 64) {
     coef[rw + k] = targets[rw + k] >= 0 ? cw : 0.0f;
     coef[rl + k] = targets[rl + k] >= 0 ? cl : 0.0f;
@@ -148,13 +147,13 @@ hipError_t launch_orpo_count(const int32_t* targets, int64_t n, int* count, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_orpo_coef(const float* lse2, const float* zt2, const int32_t* targets, int Pc,
-                            int T, int B, int p0, float beta, const int* count, float* coef,
-                            float* seq_logp, float* stage, hipStream_t s) {
+hipError_t launch_orpo_coef(const float* row_loss, const int32_t* targets, int Pc, int T, int B,
+                            int p0, float beta, const int* count, float* coef, float* seq_logp,
+                            float* stage, hipStream_t s) {
   if (Pc <= 0) return hipSuccess;
   if (T <= 0 || B <= 0 || p0 < 0 || p0 + Pc > B) return hipErrorInvalidValue;
   hipLaunchKernelGGL(orpo_coef_kernel, dim3((Pc + kWaves - 1) / kWaves), dim3(64 * kWaves), 0, s,
-                     lse2, zt2, targets, Pc, T, B, p0, beta, count, coef, seq_logp, stage);
+                     row_loss, targets, Pc, T, B, p0, beta, count, coef, seq_logp, stage);
   return hipGetLastError();
 }
 

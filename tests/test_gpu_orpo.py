@@ -87,25 +87,85 @@ def test_orpo_confident_model(flce):
     _check("orpo confident", got, exp, seq_rtol=2e-3)
 
 
-def test_orpo_certain_sequence_stays_finite(flce):
-    """A chosen sequence the model is certain of (W = 5 I, its rows h = 8 e_t:
-    logit margin 40, 1 - p ~ 1e-15) sits at the floor of the mean
-    log-probability on both sides: finite loss and gradients, equal to the
-    oracle's."""
+def test_orpo_certain_sequences(flce):
+    """Two-valued logits (W = I, a counted row h = m e_t: logit m at the
+    target, 0 elsewhere).  Pair 0 has a certain chosen sequence (margin 40:
+    1 - p ~ 1e-15) and pair 1 a certain rejected one: finite loss and
+    gradients equal to the oracle's, and each sequence's mean
+    log-probability (about -2.3e-15 for the certain ones) to its relative
+    precision: the mass of the other classes comes from fp32 sums, except
+    in the target's own 128-column slice, whose exponentials are stored in
+    bf16 (here all 127 round the same way: at most 2^-9 on half of S)."""
     B, T, H, V, beta = 2, 8, 256, 256, 0.5
-    h, _, t = _inputs(B, T, H, V, seed=58, prompt_max=2, pad_max=1)
-    W = (5.0 * torch.eye(V, H)).to(torch.bfloat16)
-    for r in range(T):
+    _, _, t = _inputs(B, T, H, V, seed=58, prompt_max=2, pad_max=1)
+    W = torch.eye(V, H).to(torch.bfloat16)
+    margin = [40.0, 10.0, 10.0, 40.0]  # chosen 0, chosen 1, rejected 0, rejected 1
+    h = torch.zeros(2 * B * T, H)
+    for r in range(2 * B * T):
         if t[r] >= 0:
-            h[r] = 0.0
-            h[r, int(t[r])] = 8.0
-    say("orpo certain sequence")
+            h[r, int(t[r])] = margin[r // T]
+    h = h.to(torch.bfloat16)
+    say("orpo certain sequences")
     got = flce.orpo_fwd_bwd(h.cuda(), W.cuda(), t.cuda(), B, T, beta, 1)
     torch.cuda.synchronize()
     exp = _oracle(h, W, t, B, T, beta)
-    assert float(got[1][0]) == -(2.0 ** -14) and exp[3][0] == -(2.0 ** -14)
-    assert torch.isfinite(got[2]).all() and torch.isfinite(got[3]).all()
-    _check("orpo certain", got, exp)
+    assert -1e-14 < exp[3][0] < 0.0 and -1e-14 < exp[3][3] < 0.0  # certain, and still < 0
+    assert all(torch.isfinite(x).all() for x in got)
+    es = float(np.max(np.abs(f64(got[1]) / exp[3] - 1.0)))
+    say(f"  seq_logp relative error {es:.2e}")
+    assert es <= 2e-3
+    _check("orpo certain", got, exp, seq_rtol=2e-3)
+
+
+def _confident_h(W, t, noise, level, rows):
+    """h for the given rows: kappa W[t] + 0.05 noise, kappa chosen so the
+    rows' mean log-probability (fp64, bf16-rounded h) is near `level`."""
+    Wd = W.double()
+    tt = t[rows].clamp(min=0).long()
+    counted = (t[rows] >= 0).numpy()
+
+    def mean_logp(kappa):
+        hh = (kappa * W[tt].float() + 0.05 * noise[rows].float()).to(torch.bfloat16).double()
+        Z = (hh @ Wd.T).numpy()
+        zt = Z[np.arange(len(rows)), tt.numpy()]
+        D = Z - zt[:, None]
+        D[np.arange(len(rows)), tt.numpy()] = -np.inf
+        return float(np.mean(-np.log1p(np.exp(D).sum(axis=1))[counted])), hh
+
+    lo, hi = 0.05, 10.0  # mean log p rises towards 0 as kappa grows
+    for _ in range(50):
+        mid = 0.5 * (lo + hi)
+        if mean_logp(mid)[0] < level:
+            lo = mid
+        else:
+            hi = mid
+    return mean_logp(0.5 * (lo + hi))[1]
+
+
+@pytest.mark.parametrize("lw,ll", [(-1e-4, -3e-4), (-3e-4, -1e-3), (-1e-3, -1e-4)])
+def test_orpo_confident_levels(flce, lw, ll):
+    """Mean log-probabilities of 1e-4 to 1e-3 below 0, where 1 - exp(l) is
+    what the odds divide by: loss, gradients and every sequence's mean
+    log-probability against the oracle at the usual tolerances."""
+    B, T, H, V, beta = 2, 64, 256, 512, 0.5
+    inp = make_random(2 * B * T, H, V, dtype="bf16", seed=60, w_std=0.3)
+    t = mask_preference_rows(inp.t, B, T, seed=60, prompt_max=8, pad_max=4)
+    h = torch.zeros(2 * B * T, H, dtype=torch.float64)
+    levels = [lw] * B + [ll] * B
+    for s_ in range(2 * B):
+        rows = torch.arange(s_ * T, (s_ + 1) * T)
+        h[rows] = _confident_h(inp.W, t, inp.h, levels[s_], rows)
+    h = h.to(torch.bfloat16)
+    say(f"orpo confident levels {lw} / {ll}")
+    got = flce.orpo_fwd_bwd(h.cuda(), inp.W.cuda(), t.cuda(), B, T, beta, 1)
+    torch.cuda.synchronize()
+    exp = _oracle(h, inp.W, t, B, T, beta)
+    lv = np.array(levels)
+    assert np.all((exp[3] / lv > 0.8) & (exp[3] / lv < 1.25)), exp[3]  # the case is as named
+    es = float(np.max(np.abs(f64(got[1]) / exp[3] - 1.0)))
+    say(f"  seq_logp relative error {es:.2e}")
+    assert es <= 1e-3
+    _check(f"orpo confident {lw}/{ll}", got, exp)
 
 
 def test_orpo_w_zero_closed_form(flce):

@@ -113,7 +113,8 @@ def test_vocab_no_hidden_allocation(flce):
     gw = torch.empty((V, H), dtype=torch.float32, device="cuda")
     need = flce.vocab_workspace_bytes(N, H, V, vc, torch.bfloat16)
     rup = lambda x: (x + 255) // 256 * 256
-    assert need == rup(rup(rup(N * vc * 2) + N * ((V + 127) // 128) * 8) + 3 * N * 4) + N * H * 4
+    # bf16 logits of a chunk, pairs, 4 floats per row, fp32 grad_h accumulator
+    assert need == rup(rup(rup(N * vc * 2) + N * ((V + 127) // 128) * 8) + 4 * N * 4) + N * H * 4
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
