@@ -32,8 +32,6 @@
 //    reused from L2 by consecutive tiles.
 #include "flce_internal.h"
 
-#include <stdlib.h>
-
 namespace flce {
 namespace {
 
@@ -342,22 +340,12 @@ hipError_t launch_layout(bool vec, const GemmArgs& g, int m_fastest, hipStream_t
   return launch_t<TileBig, A_KC, B_KC, false, EPI, OutT>(g, m_fastest, s);
 }
 
-// The direct-to-LDS pipeline is the default; FLCE_GEMM_GENERIC=1 in the
-// environment forces the register-staged kernel (for A/B comparisons).
-bool dma_enabled() {
-  static const bool on = [] {
-    const char* e = getenv("FLCE_GEMM_GENERIC");
-    return !(e && e[0] == '1');
-  }();
-  return on;
-}
-
 }  // namespace
 
-bool gemm_bf16_dma_enabled() { return dma_enabled(); }
-
+// The direct-to-LDS pipeline serves every shape it supports; this
+// register-staged kernel takes the rest.
 bool gemm_bf16_uses_dma(bool a_kc, bool b_kc, bool vec, const GemmArgs& g) {
-  return vec && dma_enabled() && gemm_bf16_dma_supported(a_kc, b_kc, g);
+  return vec && gemm_bf16_dma_supported(a_kc, b_kc, g);
 }
 
 hipError_t launch_gemm_bf16(bool a_kc, bool b_kc, int epi, bool vec,

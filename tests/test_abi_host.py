@@ -64,8 +64,17 @@ def test_workspace_bytes(lib):
     # short chunks add fp32 K-split parts of grad_h (regions 256-byte aligned):
     # 2048-row chunks of H = 4096 have 128 tiles -> 2 parts of 2048 x 4096
     rup = lambda x: (x + 255) // 256 * 256
-    assert f(8192, 4096, 128256, 2048, BF16) == \
-        rup(rup(2048 * 128256 * 2) + 2048 * 1002 * 8) + 2 * 2048 * 4096 * 4
+    base = lambda C, V: rup(rup(C * V * 2) + C * ((V + 127) // 128) * 8)
+    assert f(8192, 4096, 128256, 2048, BF16) == base(2048, 128256) + 2 * 2048 * 4096 * 4
+    # 512-row chunks of H = 4096, V = 32000 have 32 tiles (4 parts), but only
+    # 2 parts fit under 512 * 32000 * 4 bytes
+    assert f(2048, 4096, 32000, 512, BF16) == base(512, 32000) + 2 * 512 * 4096 * 4
+    assert f(2048, 1024, 32000, 512, BF16) == base(512, 32000) + 4 * 512 * 1024 * 4
+    # a vocabulary of 2^22 or more keeps fp32 logits (the exponentiated
+    # kernel addresses rows below 2^22 elements)
+    assert f(16, 64, (1 << 22) + 64, 4, BF16) == 4 * ((1 << 22) + 64) * 4
+    # so does a chunk too short for the pairs and their alignment
+    assert f(8, 64, 8, 1, BF16) == 1 * 8 * 4
     # otherwise fp32 logits of one chunk
     assert f(100, 8, 5, 1000, BF16) == 100 * 5 * 4          # chunk clamped to N
     assert f(300, 136, 1000, 100, BF16) == 100 * 1000 * 4     # H % 64 != 0
@@ -77,6 +86,22 @@ def test_workspace_bytes(lib):
     for bad in [(0, 8, 5, 1), (4, 0, 5, 1), (4, 8, 0, 1), (4, 8, 5, 0), (1 << 31, 8, 5, 1)]:
         assert f(*bad, BF16) == 0
     assert f(4, 8, 5, 1, 7) == 0
+
+
+def test_workspace_never_exceeds_one_chunk_of_fp32_logits(lib):
+    """flce_workspace_bytes(N, H, V, C) <= min(C, N) * V * 4 for every shape:
+    the bound the fused head promises against the naive N * V * 4."""
+    f = lib.flce_workspace_bytes
+    checked = 0
+    for H in (8, 64, 1024, 3584, 4096, 8192):
+        for V in (1, 8, 64, 1000, 1024, 32000, 128256, 256000):
+            for C in (1, 7, 64, 100, 512, 1024, 2048, 4096, 8192):
+                for N in sorted({C, C + 1, 2 * C, 3 * C - 5 if C > 2 else C, 16384}):
+                    for dt in (BF16, F32):
+                        need = f(N, H, V, C, dt)
+                        assert 0 < need <= min(C, N) * V * 4, (N, H, V, C, dt, need)
+                        checked += 1
+    assert checked > 4000
 
 
 P = 4096  # a 16-byte aligned stand-in address; never dereferenced below
@@ -184,7 +209,7 @@ def test_vocab_workspace_bytes(lib):
         c = min(vc, V)
         a = rup(N * c * 2)
         b = rup(a + N * ((V + 127) // 128) * 8)
-        d = rup(b + 3 * N * 4)
+        d = rup(b + 4 * N * 4)
         return d + N * H * 4
 
     for args in [(8192, 4096, 128256, 16384), (1024, 3584, 256000, 32768), (300, 128, 1024, 256),
@@ -281,7 +306,7 @@ def test_orpo_workspace_bytes(lib):
         a = rup(R * V * 2)
         b = rup(a + R * ((V + 127) // 128) * 8)
         c = rup(b + sr * H * 4)
-        d = rup(c + 4 * R * 4)
+        d = rup(c + 5 * R * 4)
         e = rup(d + R * H * 2)
         g = rup(e + R * H * 2)
         st = rup(g + R * 4)
