@@ -5,9 +5,10 @@
 
 Calls only ``synth`` (seeded inputs) and ``oracle`` (fp64 reference).  For
 each workload it stores, in ``cfg<k>_sampled.npz``: the mean loss, the
-per-row log-sum-exp of every token, a set of sampled token rows with their
-grad_h rows and a set of sampled vocabulary rows with their grad_W rows
-(gradients stored as float32).
+per-row log-sum-exp of every token, sampled token rows (at least one in
+every 256-token tile) with their grad_h rows and sampled vocabulary rows (at
+least one in every 256-row tile of W) with their grad_W rows (gradients
+stored as float32).
 """
 
 from __future__ import annotations
@@ -33,18 +34,30 @@ ORPO = dict(workload="llama3_8b_head", pairs=4, seq_len=1024, prompt_max=256, pa
             beta=0.1)
 
 
+# Output tiles of the GEMMs are 256 x 256: one sampled token row in every
+# 256-token tile and one vocabulary row in every 256-row tile of W (the
+# last, partial tile included) reach every output tile of grad_h and grad_W.
+TILE = 256
+
+
+def one_per_tile(n: int, rng) -> set:
+    return {int(rng.integers(a, min(a + TILE, n))) for a in range(0, n, TILE)}
+
+
 def sample_rows(cfg, t: np.ndarray):
-    """Token rows at both ends, at chunk edges of the benchmark's chunk and
-    a few seeded random ones; vocabulary rows at both ends, the most
-    frequent target, targets of sampled tokens and a few random ones."""
+    """Token rows: one per 256-token tile, both ends, the edges of the
+    1024-, 2048- and 4096-token chunks; vocabulary rows: one per 256-row
+    tile, both ends, the most frequent target and the targets of the first
+    and last token."""
     N, V = cfg.N, cfg.V
-    C = cfg.default_chunk
     rng = np.random.default_rng([0, 99])
-    rows = {0, 1, N // 2, N - 2, N - 1, C - 1, min(C, N - 1), 2047 % N, 2048 % N}
-    rows |= set(rng.integers(0, N, 4).tolist())
+    rows = {0, 1, N // 2, N - 2, N - 1}
+    for C in (1024, 2048, 4096, cfg.default_chunk):
+        rows |= {min(C - 1, N - 1), min(C, N - 1)}
+    rows |= one_per_tile(N, rng)
     vals, counts = np.unique(t, return_counts=True)
     vocab = {0, 1, V // 2, V - 1, int(vals[np.argmax(counts)]), int(t[0]), int(t[N - 1])}
-    vocab |= set(rng.integers(0, V, 4).tolist())
+    vocab |= one_per_tile(V, rng)
     return np.array(sorted(rows)), np.array(sorted(vocab))
 
 
@@ -87,11 +100,13 @@ def make_orpo() -> str:
     rows = {0, T - 1, T, 2 * T - 1, B * T - 1, B * T, N - 1, 2 * T, 2 * T * B // 2}
     rows |= {int(np.nonzero(t < 0)[0][0]), int(np.nonzero(t[:T] >= 0)[0][-1])}
     rows |= set(rng.integers(0, N, 5).tolist())
+    rows |= one_per_tile(N, rng)
     rows = np.array(sorted(rows))
     vals, counts = np.unique(t[t >= 0], return_counts=True)
     vocab = {0, 1, V // 2, V - 1, int(vals[np.argmax(counts)])}
-    vocab |= {int(t[r]) for r in rows if t[r] >= 0}
+    vocab |= {int(t[r]) for r in rows[:16] if t[r] >= 0}
     vocab |= set(rng.integers(0, V, 4).tolist())
+    vocab |= one_per_tile(V, rng)
     vocab = np.array(sorted(vocab))
     r = oracle.orpo_sampled(h, W, t, B, T, ORPO["beta"], rows=rows, vocab_rows=vocab,
                             chunk=1024)

@@ -188,6 +188,8 @@ def test_config2_full(flce):
     exp = oracle.flce_chunked(h64, W64, inp.t.numpy().astype(np.int64), 512)
     _check_full("cfg2", got, exp)
     say("config 2 chunk 512 vs chunk 2048")
+    # 32 grad_h tiles per chunk would take 4 K-split parts; 2 fit the bound
+    assert flce.workspace_bytes(2048, 4096, 32000, 512, torch.bfloat16) <= 512 * 32000 * 4
     got2 = flce.fwd_bwd(h, W, t, 512)
     torch.cuda.synchronize()
     _check_full("cfg2/c512", tuple(x.cpu() for x in got2), exp)
@@ -200,34 +202,47 @@ def _golden(idx):
     return np.load(p, allow_pickle=False)
 
 
+# Chunks run at full size: every workload at its benchmark chunk, and the
+# Llama-3-8B head also at 2048 and 1024 tokens, where grad_h's K = V
+# contraction is split into 2 and 4 fp32 parts.
+FULL_CHUNKS = {3: (4096, 2048, 1024), 4: (4096,), 5: (4096,)}
+
+
 @pytest.mark.parametrize("idx", [3, 4, 5])
 def test_full_size_sampled(flce, idx):
-    """Full-size workloads at the benchmark's chunk: loss and sampled rows
-    against the oracle's stored values, plus sum_j grad_W[j, :] = 0."""
+    """Full-size workloads: loss, the log-sum-exp of every token (through the
+    loss) and sampled rows (at least one token row in every 256-token tile
+    and one vocabulary row in every 256-row tile of W, last partial tiles
+    included) against the oracle's stored values, plus sum_j grad_W[j, :] = 0
+    for the whole gradient."""
     cfg = CONFIGS[idx]
     gold = _golden(idx)
+    rows_np, vrows_np = gold["rows"], gold["vocab_rows"]
+    assert set(rows_np // 256) == set(range((cfg.N + 255) // 256))
+    assert set(vrows_np // 256) == set(range((cfg.V + 255) // 256))
     say(f"config {idx} ({cfg.name}): generating inputs")
     inp = make_inputs(cfg, seed=0)
     h, W, t = to_device(inp)
     del inp
-    C = cfg.default_chunk
-    say(f"config {idx} fwd_bwd chunk={C}")
-    loss, gh, gw = flce.fwd_bwd(h, W, t, C)
-    torch.cuda.synchronize()
-    rows = torch.from_numpy(gold["rows"]).cuda()
-    vrows = torch.from_numpy(gold["vocab_rows"]).cuda()
-    el = rel(float(loss), float(gold["loss"]))
-    eh = rel_fro(f64(gh[rows]), gold["grad_h_rows"])
-    ew = rel_fro(f64(gw[vrows]), gold["grad_W_rows"])
-    colsum = gw.double().sum(dim=0).abs().max().item()
-    scale = gw.double().abs().sum(dim=0).max().item()
-    say(f"  loss {float(loss):.6f} vs {float(gold['loss']):.6f} rel {el:.2e}; "
-        f"grad_h rows rel_fro {eh:.2e}; grad_W rows rel_fro {ew:.2e}; "
-        f"|sum_j grad_W| {colsum:.2e} (sum |.| {scale:.2e})")
-    assert el <= LOSS_RTOL
-    assert eh <= GRAD_RTOL
-    assert ew <= GRAD_RTOL
-    assert colsum <= 1e-3 * scale
+    rows = torch.from_numpy(rows_np).cuda()
+    vrows = torch.from_numpy(vrows_np).cuda()
+    for C in FULL_CHUNKS[idx]:
+        say(f"config {idx} fwd_bwd chunk={C}")
+        loss, gh, gw = flce.fwd_bwd(h, W, t, C)
+        torch.cuda.synchronize()
+        el = rel(float(loss), float(gold["loss"]))
+        eh = rel_fro(f64(gh[rows]), gold["grad_h_rows"])
+        ew = rel_fro(f64(gw[vrows]), gold["grad_W_rows"])
+        colsum = gw.double().sum(dim=0).abs().max().item()
+        scale = gw.double().abs().sum(dim=0).max().item()
+        say(f"  chunk {C}: loss {float(loss):.6f} vs {float(gold['loss']):.6f} rel {el:.2e}; "
+            f"grad_h {len(rows_np)} rows rel_fro {eh:.2e}; grad_W {len(vrows_np)} rows rel_fro "
+            f"{ew:.2e}; |sum_j grad_W| {colsum:.2e} (sum |.| {scale:.2e})")
+        assert el <= LOSS_RTOL
+        assert eh <= GRAD_RTOL
+        assert ew <= GRAD_RTOL
+        assert colsum <= 1e-3 * scale
+        del loss, gh, gw
 
 
 # ---------------------------------------------------------------------------
