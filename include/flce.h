@@ -60,8 +60,13 @@ typedef enum flce_status {
   FLCE_ERR_WORKSPACE = 2,   /* workspace smaller than flce_workspace_bytes   */
   FLCE_ERR_UNSUPPORTED = 3, /* H % 8 != 0, a pointer not 16-byte aligned,
                                or a shape the entry point does not run    */
-  FLCE_ERR_HIP = 4          /* the HIP runtime reported a launch error       */
+  FLCE_ERR_HIP = 4,         /* the HIP runtime reported a launch error       */
+  FLCE_ERR_SCRATCH = 5      /* flce_fwd_bwd_noalloc: the sizes need more
+                               workspace than FLCE_NOALLOC_SCRATCH_BYTES    */
 } flce_status;
+
+/* Size of the static device scratch flce_fwd_bwd_noalloc works in. */
+#define FLCE_NOALLOC_SCRATCH_BYTES ((size_t)512 << 20)
 
 /*
  * Bytes of device workspace flce_fwd_bwd needs, with C = min(chunk, N);
@@ -396,6 +401,33 @@ flce_status flce_mfma_rate(const void* operands, int64_t operand_bytes, int64_t 
                            hipStream_t stream);
 
 /* A static, human-readable name for a status code (host only). */
+/*
+ * flce_fwd_bwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and rules as flce_fwd_bwd, minus the workspace:
+ * the call works in a static device array of FLCE_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends.
+ * Its device address is looked up once per device, on the first call with
+ * that device current (the device of `stream`); the call itself makes no
+ * hipMalloc, hipFree or other allocation.
+ *  - Returns FLCE_ERR_SCRATCH, enqueuing nothing, when
+ *    flce_workspace_bytes(N, H, V, chunk, dt) exceeds
+ *    FLCE_NOALLOC_SCRATCH_BYTES (use a smaller chunk: the Llama-3-8B head,
+ *    H = 4096 and V = 128256, fits chunks of up to 1024 tokens).
+ *  - Every call on one GPU shares that GPU's array: calls that overlap in
+ *    time on one GPU (other streams, other host threads) race and give
+ *    undefined results.  Calls serialised on one stream are safe; the
+ *    array needs no clearing between calls (every byte a call reads it
+ *    has written first).
+ *  - FLCE_ERR_HIP when the array's address cannot be obtained.
+ * This entry point keeps the per-device address as global state, unlike
+ * the others.
+ */
+flce_status flce_fwd_bwd_noalloc(const void* h, const void* W, const int32_t* targets,
+                                 int64_t N, int64_t H, int64_t V, int64_t chunk,
+                                 float* loss, void* grad_h, float* grad_W,
+                                 flce_dtype dt, hipStream_t stream);
+
 const char* flce_status_string(flce_status s);
 
 #ifdef __cplusplus

@@ -27,7 +27,11 @@ STATUS = {
     2: "FLCE_ERR_WORKSPACE",
     3: "FLCE_ERR_UNSUPPORTED",
     4: "FLCE_ERR_HIP",
+    5: "FLCE_ERR_SCRATCH",
 }
+
+# Static device scratch of flce_fwd_bwd_noalloc (FLCE_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 512 << 20
 
 # Every entry point include/flce.h declares.
 EXPORTS = (
@@ -47,6 +51,7 @@ EXPORTS = (
     "flce_orpo_fwd_bwd",
     "flce_orpo_workspace_bytes",
     "flce_mfma_rate",
+    "flce_fwd_bwd_noalloc",
     "flce_status_string",
 )
 
@@ -110,6 +115,9 @@ def load() -> ctypes.CDLL:
     lib.flce_orpo_workspace_bytes.restype = sz
     lib.flce_mfma_rate.argtypes = [vp, i64, i64, i64, vp, vp, vp]
     lib.flce_mfma_rate.restype = ctypes.c_int
+    lib.flce_fwd_bwd_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp, vp,
+                                         ctypes.c_int, vp]
+    lib.flce_fwd_bwd_noalloc.restype = ctypes.c_int
     lib.flce_status_string.argtypes = [ctypes.c_int]
     lib.flce_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -236,6 +244,26 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
     else:
         st = lib.flce_fwd_bwd_timed(*args, events.array, events.n)
     _check(st)
+    return loss, grad_h, grad_W
+
+
+def fwd_bwd_noalloc(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, chunk: int, *,
+                    loss: torch.Tensor, grad_h: torch.Tensor, grad_W: torch.Tensor,
+                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """``fwd_bwd`` through ``flce_fwd_bwd_noalloc``: no workspace argument,
+    the library's static device scratch instead, and the outputs given by
+    the caller (this function allocates nothing)."""
+    lib = load()
+    _need_cuda(h, W, targets, loss, grad_h, grad_W)
+    if targets.dtype != torch.int32:
+        raise TypeError("targets must be int32")
+    if W.dtype != h.dtype:
+        raise TypeError("h and W must share a dtype")
+    N, H = h.shape
+    V = W.shape[0]
+    _check(lib.flce_fwd_bwd_noalloc(h.data_ptr(), W.data_ptr(), targets.data_ptr(), N, H, V,
+                                    int(chunk), loss.data_ptr(), grad_h.data_ptr(),
+                                    grad_W.data_ptr(), _dt(h), _stream_ptr(h.device)))
     return loss, grad_h, grad_W
 
 

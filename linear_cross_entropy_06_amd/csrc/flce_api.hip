@@ -22,6 +22,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
@@ -807,6 +809,57 @@ extern "C" flce_status flce_mfma_rate(const void* operands, int64_t operand_byte
              : FLCE_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free entry point: flce_fwd_bwd over a static device array
+// instead of a caller-provided workspace, for callers that cannot allocate.
+// This translation unit defines no kernel, so the array's code object is
+// loaded on a device only when its address is first looked up there.
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) char scratch[FLCE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device with that device current.  In host code the array's name is a
+// host-side stand-in: only this address may reach a kernel or a copy.
+hipError_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" flce_status flce_fwd_bwd_noalloc(const void* h, const void* W,
+                                            const int32_t* targets, int64_t N, int64_t H,
+                                            int64_t V, int64_t chunk, float* loss,
+                                            void* grad_h, float* grad_W, flce_dtype dt,
+                                            hipStream_t stream) {
+  // Sizes the workspace functions reject (0) are reported by the full
+  // argument checks below; sizes beyond the array are refused here.
+  if (flce_workspace_bytes(N, H, V, chunk, dt) > FLCE_NOALLOC_SCRATCH_BYTES)
+    return FLCE_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (scratch_on_current_device(&ws) != hipSuccess) return FLCE_ERR_HIP;
+  return fwd_bwd_impl(h, W, targets, N, H, V, chunk, loss, grad_h, grad_W, ws,
+                      FLCE_NOALLOC_SCRATCH_BYTES, dt, stream, nullptr, 0, false);
+}
+
 extern "C" const char* flce_status_string(flce_status s) {
   switch (s) {
     case FLCE_OK: return "FLCE_OK";
@@ -816,6 +869,9 @@ extern "C" const char* flce_status_string(flce_status s) {
       return "FLCE_ERR_UNSUPPORTED: H % 8 != 0, a pointer not 16-byte aligned, or a shape "
              "this entry point does not run";
     case FLCE_ERR_HIP: return "FLCE_ERR_HIP: the HIP runtime reported a launch error";
+    case FLCE_ERR_SCRATCH:
+      return "FLCE_ERR_SCRATCH: these sizes need more workspace than the allocation-free "
+             "entry point's static scratch (FLCE_NOALLOC_SCRATCH_BYTES); use a smaller chunk";
   }
   return "unknown flce_status";
 }

@@ -43,7 +43,7 @@ def test_header_declares_the_boundary():
                             "flce_vocab_workspace_bytes", "flce_fwd_bwd_rmsnorm",
                             "flce_rmsnorm_workspace_bytes", "flce_orpo_fwd_bwd",
                             "flce_orpo_workspace_bytes", "flce_mfma_rate",
-                            "flce_status_string"])
+                            "flce_fwd_bwd_noalloc", "flce_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -384,8 +384,21 @@ def test_mfma_rate_validates(lib):
     assert f(P, 8192, 10, 256, P, P + 4, None) == UNSUPPORTED
 
 
+def test_noalloc_refuses_before_touching_the_device(lib):
+    """Sizes whose workspace exceeds the static scratch are refused with
+    FLCE_ERR_SCRATCH before the scratch is looked up (no device needed)."""
+    from linear_cross_entropy_06_amd import NOALLOC_SCRATCH_BYTES
+    f = lib.flce_fwd_bwd_noalloc
+    assert lib.flce_workspace_bytes(8192, 4096, 128256, 2048, BF16) > NOALLOC_SCRATCH_BYTES
+    assert lib.flce_workspace_bytes(8192, 4096, 128256, 1024, BF16) <= NOALLOC_SCRATCH_BYTES
+    assert f(P, P, P, 8192, 4096, 128256, 2048, P, P, P, BF16, None) == 5
+    assert "FLCE_NOALLOC_SCRATCH_BYTES" in lib.flce_status_string(5).decode()
+    assert "(size_t)512 << 20" in open(HEADER).read()  # the header's constant
+    assert NOALLOC_SCRATCH_BYTES == 512 << 20
+
+
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         s = lib.flce_status_string(code).decode()
         assert s.startswith("FLCE_")
     assert "unknown" in lib.flce_status_string(99).decode()
