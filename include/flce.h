@@ -76,12 +76,15 @@ typedef enum flce_status {
  *        C * V * 2 + C * ceil(V / 128) * 8   (the logits of one token chunk
  *        kept as bf16 exponentials, plus two floats per row and 128-column
  *        slice; each region rounded up to 256 bytes)
- *        + P * H * 4 when chunks are short: if a chunk of r rows gives the
- *        H x r grad_h product <= 128 tiles of 256 x 256 (and V % 64 == 0,
- *        V >= 1024 per part), its K = V contraction is split into s = 2
- *        (<= 128 tiles) or 4 (<= 64) fp32 parts, s halved until the parts
- *        fit in what remains of C * V * 4 bytes, and P is the larger of
- *        s * r over r = C and r = N mod C
+ *        + P * H * 4 when the grad_h product of a chunk of r rows (H x r,
+ *        in tiles of 256 x 256) would leave the 256 CUs partly idle: its
+ *        K = V contraction is split into s fp32 parts, s in {1, 2, 4, 8}
+ *        minimising ceil(tiles * s / 256) / s / (tiles / 256) + 560 s / V
+ *        (rounds of the chip over a perfect fill, plus the pass summing the
+ *        parts; s = 1 adds nothing), with V % 64 == 0, V >= 1024 s and the
+ *        parts within what remains of C * V * 4 bytes; P is the larger of
+ *        s * r over r = C and r = N mod C (e.g. 2 parts at H = 4096 and
+ *        2048 rows, 4 at 1024 rows, 8 at H = 3584 and 4096 rows)
  *        (when the two regions alone would exceed C * V * 4, a handful of
  *        rows of a tiny vocabulary, the second form is used)
  *   otherwise:

@@ -58,16 +58,35 @@ inline bool exp_path(int64_t H, int64_t V, flce_dtype dt) {
 // (max, sum) pairs per row on the exponentiated path.
 inline int64_t n_half_tiles(int64_t V) { return (V + flce::kHalfTile - 1) / flce::kHalfTile; }
 
-// K split of the grad_h contraction (H x rows output, K = V) when its
-// 256 x 256 tiles would not fill the chip: 4 parts for <= 64 tiles, 2 for
-// <= 128 (exponentiated path with V % 64 == 0, at least 16 slabs a part),
-// halved until the fp32 parts fit in `room` bytes (1 when none fits).
+// K split of the grad_h contraction (H x rows output, K = V: few output
+// tiles, each a long run of K slabs).  Each of s consecutive K runs is a
+// work item with its own fp32 part, summed afterwards in a fixed order.
+// The split s in {1, 2, 4, 8} minimises the estimated time relative to a
+// perfectly filled chip: the rounds of 256 CUs the tiles * s items take,
+// over s, plus the summing pass (it reads s fp32 parts at about 5 TB/s
+// while the contraction runs at about 1.4 PFLOP/s: 560 s / V of the
+// contraction's time).  V % 64 == 0, each part keeps at least 16 slabs of
+// 64 and the parts fit in `room` bytes.  At H = 4096: 64 tiles take 4 parts, 128 take
+// 2, 256 none; at H = 3584 and 4096 rows, 224 tiles take 8 (7 full
+// rounds).
+constexpr int64_t kCUs = 256;
 inline int grad_h_splits(int64_t H, int64_t rows, int64_t V, int64_t room) {
   const int64_t tiles = ((H + 255) / 256) * ((rows + 255) / 256);
-  int s = tiles <= 64 ? 4 : tiles <= 128 ? 2 : 1;
-  if (V % 64 != 0 || V / 64 < 16 * s) return 1;
-  while (s > 1 && s * rows * H * 4 > room) s /= 2;
-  return s;
+  if (V % 64 != 0) return 1;  // the split runs on the direct-to-LDS kernel only
+  int best = 1;
+  double best_t = 1e300;
+  for (int s = 1; s <= 8; s *= 2) {
+    if (s > 1 && (V / 64 < 16 * s || s * rows * H * 4 > room)) break;
+    const int64_t items = tiles * s;
+    const double rounds = static_cast<double>((items + kCUs - 1) / kCUs);
+    const double t = rounds / s / (static_cast<double>(tiles) / kCUs) +
+                     (s > 1 ? 560.0 * s / static_cast<double>(V) : 0.0);
+    if (t < best_t - 1e-9) {
+      best_t = t;
+      best = s;
+    }
+  }
+  return best;
 }
 
 // Rows of the fp32 [rows][H] part buffer the K split needs: the larger of

@@ -2,8 +2,9 @@
 //
 // Same contract as the generic kernel in gemm_bf16.hip (D[m][n] =
 // sum_k A(m,k) B(n,k), stored as out[n * ldo + m]) for the shapes the
-// loss head runs at scale: K a multiple of 64, every contiguous extent and
-// leading dimension a multiple of 8 elements, 16-byte aligned bases.
+// loss head runs at scale: K a multiple of 64 unless both operands are
+// m-contiguous, every contiguous extent and leading dimension a multiple of
+// 8 elements, 16-byte aligned bases.
 //
 // CDNA4 design:
 //  * 256x256 output tile per 256-thread workgroup; each wave64 owns a
@@ -128,6 +129,7 @@ struct DmaOperand {
   int64_t kstep;               // bytes to advance per k slab
   int start = 0;               // first K slab of this tile (rotation)
   int kt_total = 1;            // K slabs
+  int tail_range = kBufferRange;  // buffer range of the last slab (bytes)
 
   __device__ __forceinline__ void init(const uint16_t* ptr, int64_t ld, int row0,
                                        int rows_total, int wave, int lane) {
@@ -156,12 +158,22 @@ struct DmaOperand {
     kstep = KC ? (int64_t)kBK * 2 : (int64_t)kBK * ld * 2;
   }
 
-  // Request slab kt (before rotation) into `slot`.
+  // K % 64 valid k rows in the last slab (m-contiguous operands; 0: full).
+  __device__ __forceinline__ void set_tail(int ktail, int64_t ld) {
+    if (!KC && ktail != 0) tail_range = (int)((int64_t)ktail * ld * 2);
+  }
+
+  // Request slab kt (before rotation) into `slot`.  A partial last slab
+  // (m-contiguous operands only, K % 64 != 0) gets a buffer range that ends
+  // at its last valid k row: the pieces of later rows lie beyond it, and
+  // the hardware's range check returns zeros for them (no memory is read),
+  // so the missing k contribute exact zeros to the products.
   __device__ __forceinline__ void issue(int kt, char* slot, int wave) const {
     kt += start;
     if (kt >= kt_total) kt -= kt_total;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(base + kt * kstep), (short)0, kBufferRange, kBufferFlags);
+        const_cast<char*>(base + kt * kstep), (short)0,
+        kt == kt_total - 1 ? tail_range : kBufferRange, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < kDmaPerOp; ++i) {
       const int b = kDmaPerOp * wave + i;
@@ -303,11 +315,15 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
   // K split (fp32 part stores only): workgroup row blockIdx.y takes its own
   // run of slabs and its own output slice.  Compiled out of the other
   // epilogues, whose register budget has no room for it.
-  int KT = g.K / kBK;
+  // K slabs, the last one partial when K % 64 != 0 (its missing k read as
+  // zeros).
+  int KT = (g.K + kBK - 1) / kBK;
+  int ktail = g.K % kBK;
   if (kSplitK<EPI> && g.splits > 1) {
     const int per = (KT + g.splits - 1) / g.splits;
     const int kt0 = (int)blockIdx.y * per;
-    KT = min(per, KT - kt0);  // >= 1: checked on the host
+    if (kt0 + per < KT) ktail = 0;  // only the last part holds the partial slab
+    KT = min(per, KT - kt0);        // >= 1: checked on the host
     const int64_t k0 = (int64_t)kt0 * kBK;
     g.A = static_cast<const uint16_t*>(g.A) + (A_KC ? k0 : k0 * g.lda);
     g.B = static_cast<const uint16_t*>(g.B) + (B_KC ? k0 : k0 * g.ldb);
@@ -334,6 +350,8 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   da.kt_total = db.kt_total = KT;
+  da.set_tail(ktail, g.lda);
+  db.set_tail(ktail, g.ldb);
   da.start = db.start = __builtin_amdgcn_readfirstlane(
       g.stagger > 0 ? (int)(((unsigned)grp * (unsigned)g.stagger) % (unsigned)KT) : 0);
   // Prologue: A_0 -> slot 0, B_0 -> slot 1, A_1 -> slot 2; wait for the
@@ -636,7 +654,12 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
 }  // namespace
 
 bool gemm_bf16_dma_supported(bool a_kc, bool b_kc, const GemmArgs& g) {
-  if (g.K <= 0 || g.K % kBK != 0 || g.M <= 0 || g.N <= 0) return false;
+  if (g.K <= 0 || g.M <= 0 || g.N <= 0) return false;
+  // K % 64 != 0 (a partial last slab, zero-filled through the buffer
+  // range) needs both operands m-contiguous, whose slab offsets grow with
+  // the k row; the last slab's range (rows x leading dimension) stays
+  // below 2^31 bytes.
+  if (g.K % kBK != 0 && (a_kc || b_kc)) return false;
   // m runs of 8 (stores, m-contiguous A chunks); n runs of 8 only when B
   // is n-contiguous.
   if (g.M % 8 != 0 || (!b_kc && g.N % 8 != 0)) return false;
@@ -647,13 +670,12 @@ bool gemm_bf16_dma_supported(bool a_kc, bool b_kc, const GemmArgs& g) {
   // fp32 epilogue offsets within a wave's 128 output rows are 32-bit.
   if (g.ldo >= (int64_t{1} << 22)) return false;
   if (g.splits > 1) {  // every part gets at least one slab
-    const int kt = g.K / kBK, per = (kt + g.splits - 1) / g.splits;
+    const int kt = (g.K + kBK - 1) / kBK, per = (kt + g.splits - 1) / g.splits;
     if ((g.splits - 1) * per >= kt || g.splits > 65535) return false;
   }
   const uintptr_t al = reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B) |
                        reinterpret_cast<uintptr_t>(g.out);
   if (al & 15u) return false;
-  (void)a_kc;
   return true;
 }
 

@@ -2,6 +2,7 @@
 
     python tests/golden/make_golden.py [config ...]      (default: 2 3 4 5)
     python tests/golden/make_golden.py orpo              (preference batch)
+    python tests/golden/make_golden.py ragged            (workload 3, 8100 tokens)
 
 Calls only ``synth`` (seeded inputs) and ``oracle`` (fp64 reference).  For
 each workload it stores, in ``cfg<k>_sampled.npz``: the mean loss, the
@@ -85,6 +86,44 @@ def make(idx: int) -> str:
     return out
 
 
+# Workload 3 cut to its first 8100 tokens: at the benchmark's 4096-token
+# chunk the last chunk has 4004 rows, so grad_W's contraction length is not
+# a multiple of 64 (a partial last slab).
+RAGGED = dict(idx=3, N=8100)
+
+
+def make_ragged() -> str:
+    cfg = CONFIGS[RAGGED["idx"]]
+    N = RAGGED["N"]
+    t0 = time.perf_counter()
+    x = make_inputs(cfg, seed=0)
+    h, W, t = to_float64(x.h[:N]), to_float64(x.W), x.t[:N].numpy().astype(np.int64)
+    V = cfg.V
+    rng = np.random.default_rng([0, 97])
+    rows = {0, N - 1, 4095, 4096, 4097, N - 2} | one_per_tile(N, rng)
+    # every 4th 256-row tile of W, the last one included, and the targets of
+    # the last chunk's first and last token
+    vocab = {int(rng.integers(a, min(a + TILE, V))) for a in range(0, V, 4 * TILE)}
+    vocab |= {V - 1, int(t[4096]), int(t[N - 1])}
+    rows, vocab = np.array(sorted(rows)), np.array(sorted(vocab))
+    r = oracle.flce_sampled(h, W, t, rows=rows, vocab_rows=vocab, chunk=1024)
+    out = os.path.join(HERE, f"cfg{RAGGED['idx']}_n{N}_sampled.npz")
+    np.savez_compressed(
+        out,
+        config=np.array(cfg.name),
+        seed=np.array(0),
+        tokens=np.array(N),
+        loss=np.array(r["loss"]),
+        rows=rows,
+        vocab_rows=vocab,
+        grad_h_rows=r["grad_h_rows"].astype(np.float32),
+        grad_W_rows=r["grad_W_rows"].astype(np.float32),
+    )
+    print(f"cfg{RAGGED['idx']} first {N} tokens: loss={r['loss']:.9f} rows={len(rows)} "
+          f"vocab_rows={len(vocab)} ({time.perf_counter() - t0:.1f} s) -> {out}", flush=True)
+    return out
+
+
 def make_orpo() -> str:
     cfg = config_by_name(ORPO["workload"])
     B, T = ORPO["pairs"], ORPO["seq_len"]
@@ -135,4 +174,9 @@ def make_orpo() -> str:
 if __name__ == "__main__":
     args = sys.argv[1:] or ["2", "3", "4", "5"]
     for a in args:
-        make_orpo() if a == "orpo" else make(int(a))
+        if a == "orpo":
+            make_orpo()
+        elif a == "ragged":
+            make_ragged()
+        else:
+            make(int(a))

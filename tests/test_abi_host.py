@@ -54,12 +54,36 @@ def test_library_exports_every_declared_symbol(lib):
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
 
+def _grad_h_splits(H, rows, V, room):
+    """The K split rule of grad_h as the header documents it."""
+    tiles = ((H + 255) // 256) * ((rows + 255) // 256)
+    if V % 64:
+        return 1
+    best, best_t = 1, float("inf")
+    for s in (1, 2, 4, 8):
+        if s > 1 and (V // 64 < 16 * s or s * rows * H * 4 > room):
+            break
+        items = tiles * s
+        t = -(-items // 256) / s / (tiles / 256) + (560.0 * s / V if s > 1 else 0.0)
+        if t < best_t - 1e-9:
+            best, best_t = s, t
+    return best
+
+
+def test_grad_h_split_rule():
+    assert _grad_h_splits(4096, 4096, 128256, 1 << 40) == 1   # 256 tiles
+    assert _grad_h_splits(4096, 2048, 128256, 1 << 40) == 2   # 128 tiles
+    assert _grad_h_splits(4096, 1024, 128256, 1 << 40) == 4   # 64 tiles
+    assert _grad_h_splits(3584, 4096, 256000, 1 << 40) == 8   # 224 tiles: 7 full rounds
+    assert _grad_h_splits(4096, 2048, 32000, 1 << 40) == 2
+    assert _grad_h_splits(3584, 4096, 256000, 0) == 1          # no room
+
+
 def test_workspace_bytes(lib):
     f = lib.flce_workspace_bytes
     # bf16 with H % 64 == 0 and V % 8 == 0: exponentiated bf16 logits of one
     # chunk plus two floats per row and 128-column half tile
     assert f(8192, 4096, 128256, 4096, BF16) == 4096 * 128256 * 2 + 4096 * 1002 * 8
-    assert f(8192, 3584, 256000, 4096, BF16) == 4096 * 256000 * 2 + 4096 * 2000 * 8
     assert f(300, 128, 1000, 128, BF16) == 128 * 1000 * 2 + 128 * 8 * 8
     # short chunks add fp32 K-split parts of grad_h (regions 256-byte aligned):
     # 2048-row chunks of H = 4096 have 128 tiles -> 2 parts of 2048 x 4096
@@ -69,7 +93,10 @@ def test_workspace_bytes(lib):
     # 512-row chunks of H = 4096, V = 32000 have 32 tiles (4 parts), but only
     # 2 parts fit under 512 * 32000 * 4 bytes
     assert f(2048, 4096, 32000, 512, BF16) == base(512, 32000) + 2 * 512 * 4096 * 4
-    assert f(2048, 1024, 32000, 512, BF16) == base(512, 32000) + 4 * 512 * 1024 * 4
+    # 8 tiles at H = 1024: 8 parts
+    assert f(2048, 1024, 32000, 512, BF16) == base(512, 32000) + 8 * 512 * 1024 * 4
+    # H = 3584 at 4096 rows: 224 tiles -> 8 parts (1792 items, 7 full rounds)
+    assert f(8192, 3584, 256000, 4096, BF16) == base(4096, 256000) + 8 * 4096 * 3584 * 4
     # a vocabulary of 2^22 or more keeps fp32 logits (the exponentiated
     # kernel addresses rows below 2^22 elements)
     assert f(16, 64, (1 << 22) + 64, 4, BF16) == 4 * ((1 << 22) + 64) * 4
@@ -294,9 +321,7 @@ def test_orpo_workspace_bytes(lib):
     rup = lambda x: (x + 255) // 256 * 256
 
     def splits(H, rows, V):
-        tiles = ((H + 255) // 256) * ((rows + 255) // 256)
-        s = 4 if tiles <= 64 else 2 if tiles <= 128 else 1
-        return s if (V % 64 == 0 and V // 64 >= 16 * s) else 1
+        return _grad_h_splits(H, rows, V, float("inf"))
 
     def formula(B, T, H, V, cp):
         pc = min(cp, B)

@@ -245,6 +245,36 @@ def test_full_size_sampled(flce, idx):
         del loss, gh, gw
 
 
+def test_full_size_ragged_last_chunk(flce):
+    """The Llama-3-8B head on its first 8100 tokens at the 4096-token chunk:
+    the last chunk has 4004 rows, so grad_W's contraction ends in a partial
+    slab of 36 rows (zero-filled on the direct-to-LDS path).  Loss and
+    sampled rows (one token row per 256-token tile, one vocabulary row per
+    four 256-row tiles of W) against the oracle's stored values, plus
+    sum_j grad_W[j, :] = 0."""
+    gold = np.load(os.path.join(GOLDEN, "cfg3_n8100_sampled.npz"), allow_pickle=False)
+    cfg = CONFIGS[3]
+    N = int(gold["tokens"])
+    say(f"config 3, first {N} tokens: generating inputs")
+    inp = make_inputs(cfg, seed=0)
+    h, W, t = inp.h[:N].contiguous().cuda(), inp.W.cuda(), inp.t[:N].contiguous().cuda()
+    del inp
+    say(f"config 3 first {N} tokens fwd_bwd chunk=4096 (last chunk {N - 4096} rows)")
+    loss, gh, gw = flce.fwd_bwd(h, W, t, 4096)
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(gold["rows"]).cuda()
+    vrows = torch.from_numpy(gold["vocab_rows"]).cuda()
+    el = rel(float(loss), float(gold["loss"]))
+    eh = rel_fro(f64(gh[rows]), gold["grad_h_rows"])
+    ew = rel_fro(f64(gw[vrows]), gold["grad_W_rows"])
+    colsum = gw.double().sum(dim=0).abs().max().item()
+    scale = gw.double().abs().sum(dim=0).max().item()
+    say(f"  loss rel {el:.2e}; grad_h rows rel_fro {eh:.2e}; grad_W rows rel_fro {ew:.2e}; "
+        f"|sum_j grad_W| {colsum:.2e} (sum |.| {scale:.2e})")
+    assert el <= LOSS_RTOL and eh <= GRAD_RTOL and ew <= GRAD_RTOL
+    assert colsum <= 1e-3 * scale
+
+
 # ---------------------------------------------------------------------------
 # closed forms, invariants, determinism, memory
 # ---------------------------------------------------------------------------
@@ -305,9 +335,9 @@ def test_no_hidden_allocation(flce):
     gw = torch.empty((V, H), dtype=torch.float32, device="cuda")
     need = flce.workspace_bytes(N, H, V, C, torch.bfloat16)
     # bf16 exponentiated logits of one chunk + (max, sum) per 128-column half
-    # tile + fp32 K-split parts of grad_h (8 tiles of 256 x 256 -> 4 parts)
+    # tile + fp32 K-split parts of grad_h (8 tiles of 256 x 256 -> 8 parts)
     rup = lambda x: (x + 255) // 256 * 256
-    assert need == rup(rup(C * V * 2) + C * (V // 128 + (V % 128 > 0)) * 8) + 4 * C * H * 4
+    assert need == rup(rup(C * V * 2) + C * (V // 128 + (V % 128 > 0)) * 8) + 8 * C * H * 4
     assert need <= C * V * 4 < cfg.naive_logits_bytes
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
