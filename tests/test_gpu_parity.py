@@ -374,6 +374,28 @@ def test_large_logits_stress(flce):
     assert el <= LOSS_RTOL and eh <= GRAD_RTOL and ew <= GRAD_RTOL
 
 
+def test_vocabulary_beyond_2_22_takes_the_fp32_path(flce):
+    """V = 2^22 + 64 bf16: the exponentiated kernel addresses rows below 2^22
+    elements, so the head keeps fp32 logits (workspace C * V * 4) and must
+    still match the oracle, instead of failing at launch."""
+    N, H, V, C = 16, 64, (1 << 22) + 64, 8
+    assert flce.workspace_bytes(N, H, V, C, torch.bfloat16) == C * V * 4
+    inp = make_random(N, H, V, dtype="bf16", seed=12, w_std=0.3)
+    h, W, t = to_device(inp)
+    say(f"flce_fwd_bwd N={N} H={H} V={V} chunk={C} (fp32 logits path)")
+    loss, gh, gw = flce.fwd_bwd(h, W, t, C)
+    torch.cuda.synchronize()
+    hh, WW = to_float64(inp.h), to_float64(inp.W)
+    tt = inp.t.numpy().astype(np.int64)
+    vrows = np.unique(np.concatenate([tt, [0, 1, V // 2, V - 1]]))
+    r = oracle.flce_sampled(hh, WW, tt, rows=np.arange(N), vocab_rows=vrows, chunk=8)
+    el = rel(float(loss), r["loss"])
+    eh = rel_fro(f64(gh), r["grad_h_rows"])
+    ew = rel_fro(f64(gw[torch.from_numpy(vrows).cuda()]), r["grad_W_rows"])
+    say(f"  loss rel {el:.2e} grad_h rel_fro {eh:.2e} grad_W rows rel_fro {ew:.2e}")
+    assert el <= LOSS_RTOL and eh <= GRAD_RTOL and ew <= GRAD_RTOL
+
+
 def test_out_of_range_target_is_nan_not_a_fault(flce):
     inp = make_random(8, 16, 50, dtype="bf16", seed=10)
     h, W, t = to_device(inp)
