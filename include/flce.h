@@ -410,9 +410,11 @@ flce_status flce_mfma_rate(const void* operands, int64_t operand_bytes, int64_t 
  * Same arguments, results and rules as flce_fwd_bwd, minus the workspace:
  * the call works in a static device array of FLCE_NOALLOC_SCRATCH_BYTES
  * that the library holds on every GPU it runs on until the process ends.
- * Its device address is looked up once per device, on the first call with
- * that device current (the device of `stream`); the call itself makes no
- * hipMalloc, hipFree or other allocation.
+ * Its address on a device is looked up once, on the first call whose
+ * `stream` belongs to that device (the current device for the null
+ * stream), with that device made current for the lookup and the caller's
+ * current device restored; no call makes a hipMalloc, hipFree or other
+ * allocation.
  *  - Returns FLCE_ERR_SCRATCH, enqueuing nothing, when
  *    flce_workspace_bytes(N, H, V, chunk, dt) exceeds
  *    FLCE_NOALLOC_SCRATCH_BYTES (use a smaller chunk: the Llama-3-8B head,

@@ -842,18 +842,31 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mutex;
 void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device
 
-// Device address of the current device's copy of `scratch`, looked up once
-// per device with that device current.  In host code the array's name is a
+// Device address of `scratch` on the device that `stream` belongs to (the
+// current device for the null stream), looked up once per device with that
+// device current and restored afterwards.  In host code the array's name is a
 // host-side stand-in: only this address may reach a kernel or a copy.
-hipError_t scratch_on_current_device(void** out) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
+hipError_t scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd = -1;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return e;
+    dev = static_cast<int>(sd);
+  }
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_scratch_mutex);
   if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
     if (e != hipSuccess) return e;
     if (!p) return hipErrorInvalidSymbol;
     g_scratch_ptr[dev] = p;
@@ -874,7 +887,7 @@ extern "C" flce_status flce_fwd_bwd_noalloc(const void* h, const void* W,
   if (flce_workspace_bytes(N, H, V, chunk, dt) > FLCE_NOALLOC_SCRATCH_BYTES)
     return FLCE_ERR_SCRATCH;
   void* ws = nullptr;
-  if (scratch_on_current_device(&ws) != hipSuccess) return FLCE_ERR_HIP;
+  if (scratch_for_stream(stream, &ws) != hipSuccess) return FLCE_ERR_HIP;
   return fwd_bwd_impl(h, W, targets, N, H, V, chunk, loss, grad_h, grad_W, ws,
                       FLCE_NOALLOC_SCRATCH_BYTES, dt, stream, nullptr, 0, false);
 }

@@ -11,6 +11,7 @@
 
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
+typedef int hipDevice_t;
 
 typedef enum hipError_t {
   hipSuccess = 0,
@@ -34,6 +35,8 @@ hipError_t hipEventRecord(hipEvent_t event, hipStream_t stream);
 hipError_t hipMemcpyAsync(void* dst, const void* src, size_t bytes, hipMemcpyKind kind,
                           hipStream_t stream);
 hipError_t hipGetDevice(int* device);
+hipError_t hipSetDevice(int device);
+hipError_t hipStreamGetDevice(hipStream_t stream, hipDevice_t* device);
 hipError_t hipGetSymbolAddress(void** dev_ptr, const void* symbol);
 #ifdef __cplusplus
 }

@@ -101,6 +101,11 @@ hipError_t hipGetDevice(int* device) {
   *device = 0;
   return hipSuccess;
 }
+hipError_t hipSetDevice(int device) { return device == 0 ? hipSuccess : hipErrorInvalidDevice; }
+hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t* device) {
+  *device = 0;
+  return hipSuccess;
+}
 // The host stand-in of a device symbol is its own address; the scratch the
 // allocation-free entry point asks for counts as a buffer from then on (the
 // library looks it up once per device, so it survives flce_stub_reset).

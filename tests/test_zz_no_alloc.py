@@ -27,7 +27,7 @@ def flce():
     return m
 
 
-def _run_both(flce, N, H, V, chunk, seed, w_std=0.1):
+def _run_both(flce, N, H, V, chunk, seed, w_std=0.1, stream=None):
     inp = make_random(N, H, V, dtype="bf16", seed=seed, w_std=w_std)
     h, W, t = inp.h.cuda(), inp.W.cuda(), inp.t.cuda()
     say(f"flce_fwd_bwd N={N} H={H} V={V} chunk={chunk}")
@@ -39,8 +39,14 @@ def _run_both(flce, N, H, V, chunk, seed, w_std=0.1):
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base = torch.cuda.max_memory_allocated()
-    say(f"flce_fwd_bwd_noalloc N={N} H={H} V={V} chunk={chunk}")
-    got = flce.fwd_bwd_noalloc(h, W, t, chunk, loss=loss, grad_h=gh, grad_W=gw)
+    say(f"flce_fwd_bwd_noalloc N={N} H={H} V={V} chunk={chunk} "
+        f"{'side' if stream is not None else 'current'} stream")
+    if stream is not None:
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            got = flce.fwd_bwd_noalloc(h, W, t, chunk, loss=loss, grad_h=gh, grad_W=gw)
+    else:
+        got = flce.fwd_bwd_noalloc(h, W, t, chunk, loss=loss, grad_h=gh, grad_W=gw)
     torch.cuda.synchronize()
     assert torch.cuda.max_memory_allocated() == base  # nothing allocated by the call
     el = rel(float(got[0]), float(ref[0]))
@@ -58,6 +64,13 @@ def test_noalloc_matches_fwd_bwd_twice_second_smaller(flce):
     # must not leak into the second
     _run_both(flce, 2048, 1024, 32000, 1024, seed=70)
     _run_both(flce, 300, 128, 1000, 128, seed=71, w_std=0.3)
+
+
+def test_noalloc_on_a_side_stream(flce):
+    # a stream other than the null stream: the scratch is looked up on the
+    # stream's device, and the call is ordered on that stream
+    side = torch.cuda.Stream()
+    _run_both(flce, 1000, 256, 4096, 256, seed=72, w_std=0.2, stream=side)
 
 
 def test_noalloc_refuses_sizes_beyond_the_scratch(flce):
