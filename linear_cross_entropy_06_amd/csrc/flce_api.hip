@@ -1,6 +1,7 @@
 // C ABI of the fused linear + cross-entropy head: argument checks, the token
-// chunk loop and the kernel launches.  Host code only; nothing here
-// allocates, synchronises or reads device memory.
+// chunk loop and the kernel launches.  Host code, plus the one static device
+// array of the allocation-free entry point at the end of the file; nothing
+// here allocates, synchronises or reads device memory.
 //
 // Per token chunk of C rows (page 1, "Liger Kernel explained", section
 // "What does Liger Kernel actually fuse": only a chunk of logits is ever
