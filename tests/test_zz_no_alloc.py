@@ -6,7 +6,8 @@ so their outputs must agree bit for bit (a stricter form of the parity bar:
 loss relative error <= 1e-3, gradients relative Frobenius error <= 1e-2).
 Two calls in a row, the second on a smaller input, check that the scratch
 keeps no state that a later call depends on; the calls make no allocation
-through torch's allocator, and sizes beyond the scratch are refused.
+through torch's allocator, a side stream and a captured HIP graph give the
+same bits, and sizes beyond the scratch are refused.
 """
 
 import pytest
@@ -71,6 +72,47 @@ def test_noalloc_on_a_side_stream(flce):
     # stream's device, and the call is ordered on that stream
     side = torch.cuda.Stream()
     _run_both(flce, 1000, 256, 4096, 256, seed=72, w_std=0.2, stream=side)
+
+
+def test_noalloc_under_graph_capture(flce):
+    # the callers this entry point is for: one call captured into a HIP graph
+    # (nothing allocated while capturing), replayed several times with eager
+    # work and synchronisations in between; every replay equals the eager
+    # call bit for bit, and a replay after the inputs change in place follows
+    # the new inputs
+    N, H, V, chunk = 1000, 256, 4096, 256
+    a = make_random(N, H, V, dtype="bf16", seed=73, w_std=0.2)
+    b = make_random(N, H, V, dtype="bf16", seed=74, w_std=0.2)
+    h, W, t = a.h.cuda(), a.W.cuda(), a.t.cuda()
+    refs = []
+    for inp in (a, b):
+        say(f"flce_fwd_bwd (eager reference) N={N} H={H} V={V} chunk={chunk}")
+        refs.append(tuple(x.clone() for x in flce.fwd_bwd(inp.h.cuda(), inp.W.cuda(),
+                                                          inp.t.cuda(), chunk)))
+    loss = torch.empty((), dtype=torch.float32, device="cuda")
+    gh = torch.empty_like(h)
+    gw = torch.empty((V, H), dtype=torch.float32, device="cuda")
+    say("flce_fwd_bwd_noalloc eager warm-up (looks up the scratch address)")
+    flce.fwd_bwd_noalloc(h, W, t, chunk, loss=loss, grad_h=gh, grad_W=gw)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say("flce_fwd_bwd_noalloc captured into a graph")
+    with torch.cuda.graph(graph):
+        flce.fwd_bwd_noalloc(h, W, t, chunk, loss=loss, grad_h=gh, grad_W=gw)
+    torch.cuda.synchronize()
+    for rep, which in enumerate((0, 0, 1, 0)):
+        src = (a, b)[which]
+        h.copy_(src.h.cuda())
+        W.copy_(src.W.cuda())
+        t.copy_(src.t.cuda())
+        for x in (loss, gh, gw):
+            x.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say(f"graph replay {rep} (inputs {'ab'[which]})")
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((loss, gh, gw), refs[which]):
+            assert torch.equal(got, want)
 
 
 def test_noalloc_refuses_sizes_beyond_the_scratch(flce):
