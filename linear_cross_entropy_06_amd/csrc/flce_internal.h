@@ -99,7 +99,10 @@ hipError_t launch_ce_rows_bf16(uint16_t* z, int64_t ldz, const int32_t* targets,
 // W[targets[i]] (bf16 rows of H elements, fp32 accumulation); the row loss
 // is ln(1 + S) with S = sum over j != t of exp(z_j - z_t), formed from the
 // other half tiles' pairs and the target's half tile's u values without the
-// target (positive terms only), and G[i, t] = -S / (1 + S) * scale.
+// target (positive terms only), and G[i, t] = -S / (1 + S) * scale.  Two
+// launches: the row statistics, staged per row as loss, lse2 and pt1 at
+// row_loss[i * loss_stride + 0, 1, 2] (loss_stride >= 3), then the
+// elementwise rewrite in memory order.
 hipError_t launch_ce_rows_exp(uint16_t* u, int64_t ldu, const float* row_part, int64_t ldp,
                               const uint16_t* h, const uint16_t* W, int H,
                               const int32_t* targets, int rows, int V, float scale,

@@ -160,7 +160,7 @@ hipError_t launch_ce_rows_exp(uint16_t* u, int64_t ldu, const float* row_part, i
   need(h, int64_t{rows} * H * 2, "ce_rows_exp h");
   need(W, int64_t{V} * H * 2, "ce_rows_exp W");
   need(targets, rows * int64_t{4}, "ce_rows_exp targets");
-  need(row_loss, ((rows - 1) * loss_stride + 1) * 4, "ce_rows_exp loss");
+  need(row_loss, ((rows - 1) * loss_stride + 3) * 4, "ce_rows_exp loss, lse2, pt1");
   return hipSuccess;
 }
 hipError_t launch_ce_target_mass(const uint16_t* u, int64_t ldu, const int32_t* targets, int rows,
