@@ -562,15 +562,28 @@ ce_rows_bf16_kernel(uint16_t* __restrict__ z, int64_t ldz, const int32_t* __rest
   }
 }
 
-constexpr int kSumThreads = 256;
+constexpr int kSumThreads = 1024;
 
+// Thread j adds rows j, j + 1024, ... in that order (four loads in flight:
+// the staged losses sit a row of grad_h apart, one cache line each), then
+// a fixed tree combines the threads.
 __global__ void __launch_bounds__(kSumThreads)
 loss_sum_kernel(const float* __restrict__ row_loss, int64_t loss_stride, int rows,
                 float scale, int first, float* __restrict__ loss) {
   __shared__ double part[kSumThreads];
   double acc = 0.0;
-  for (int i = threadIdx.x; i < rows; i += kSumThreads)
-    acc += (double)row_loss[(int64_t)i * loss_stride];
+  int i = threadIdx.x;
+  for (; i + 3 * kSumThreads < rows; i += 4 * kSumThreads) {
+    const float a0 = row_loss[(int64_t)i * loss_stride];
+    const float a1 = row_loss[(int64_t)(i + kSumThreads) * loss_stride];
+    const float a2 = row_loss[(int64_t)(i + 2 * kSumThreads) * loss_stride];
+    const float a3 = row_loss[(int64_t)(i + 3 * kSumThreads) * loss_stride];
+    acc += (double)a0;
+    acc += (double)a1;
+    acc += (double)a2;
+    acc += (double)a3;
+  }
+  for (; i < rows; i += kSumThreads) acc += (double)row_loss[(int64_t)i * loss_stride];
   part[threadIdx.x] = acc;
   __syncthreads();
   for (int w = kSumThreads / 2; w >= 1; w >>= 1) {

@@ -53,6 +53,10 @@ def main(lib_path: str) -> int:
               (8100, 4096, 128256, 4096), (8192, 4096, 128256, 1024),
               (8192, 3584, 256000, 4096), (16384, 4096, 128256, 4096), (64, 64, 40000, 64),
               (7, 128, 1000, 3), (16, 64, (1 << 22) + 64, 4)]
+    # the seeded shapes of the GPU parity sweep as well
+    sys.path.insert(0, "tests")
+    from parity_util import random_shapes
+    shapes += sorted({(N, H, V, C) for N, H, V, C, _ in random_shapes()})
     for (N, H, V, C), dt in itertools.product(shapes, (BF16, F32)):
         es = 2 if dt == BF16 else 4
         need = lib.flce_workspace_bytes(N, H, V, C, dt)

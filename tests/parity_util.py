@@ -54,3 +54,28 @@ def bf16_rows_from_workspace(z: torch.Tensor, rows: int, V: int) -> np.ndarray:
 
 def to_device(inp, device="cuda"):
     return (inp.h.to(device), inp.W.to(device), inp.t.to(device))
+
+
+def random_shapes(seed: int = 2026, count: int = 32):
+    """Seeded (N, H, V, chunk, dtype) cases spread over the shape rules the
+    library switches on: H a multiple of 64 or only of 8, V a multiple of 64,
+    of 8 or neither, chunks that divide N or leave a ragged last chunk,
+    single-row chunks, bf16 and fp32.  Sizes stay small enough for the fp64
+    oracle to take about a second a case."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        N = int(np.exp(rng.uniform(0.0, np.log(1500.0))))
+        H = 8 * int(rng.integers(1, 65))
+        if rng.random() < 0.5:
+            H = 64 * max(1, H // 64)
+        V = int(np.exp(rng.uniform(0.0, np.log(9000.0))))
+        r = rng.random()
+        if r < 0.25:
+            V = 64 * max(1, V // 64)
+        elif r < 0.5:
+            V = 8 * max(1, V // 8)
+        chunk = int(rng.integers(1, N + 1))
+        dtype = "f32" if rng.random() < 0.2 else "bf16"
+        out.append((max(N, 1), H, max(V, 1), chunk, dtype))
+    return out

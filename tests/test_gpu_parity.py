@@ -17,7 +17,7 @@ import torch
 import oracle
 from synth import CONFIGS, make_inputs, make_random, to_float64
 from parity_util import (GRAD_RTOL, LOSS_RTOL, bf16_rows_from_workspace, f64, rel,
-                         rel_fro, say, to_device)
+                         rel_fro, say, to_device, random_shapes)
 
 pytestmark = pytest.mark.gpu
 
@@ -158,6 +158,23 @@ def test_fwd_bwd_small(flce, N, H, V, chunk, dtype):
         assert f64(got[1]).max() == 0 and np.abs(f64(got[2])).max() == 0
         return
     _check_full(f"small{(N, H, V, chunk, dtype)}", got, exp)
+
+
+@pytest.mark.parametrize("N,H,V,chunk,dtype", random_shapes())
+def test_fwd_bwd_random_shapes(flce, N, H, V, chunk, dtype):
+    # seeded shapes across the rules the library switches on (exponentiated
+    # or fp32 logits, direct-to-LDS or register-staged GEMMs, K splits,
+    # ragged chunks and tiles)
+    inp = make_random(N, H, V, dtype=dtype, seed=7 * N + 3 * V + H, w_std=0.3)
+    h, W, t = to_device(inp)
+    say(f"flce_fwd_bwd random shape N={N} H={H} V={V} chunk={chunk} {dtype}")
+    got = flce.fwd_bwd(h, W, t, chunk)
+    torch.cuda.synchronize()
+    if V == 1:
+        assert abs(float(got[0])) < 1e-6
+        assert f64(got[1]).max() == 0 and np.abs(f64(got[2])).max() == 0
+        return
+    _check_full(f"random{(N, H, V, chunk, dtype)}", got, _oracle(inp))
 
 
 def test_config1_fp32(flce):
