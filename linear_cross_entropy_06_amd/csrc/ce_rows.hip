@@ -485,9 +485,8 @@ ce_stats_exp_kernel(const float* __restrict__ row_part, int64_t ldp, const float
 // Cross entropy of given bf16 logit rows (the standalone loss on logits):
 // pass 1 online (max, sum) over the row, pass 2 rewrites every logit in
 // place with (2^(y - lse2) - [j == t]) * scale in bf16 (same place, same
-// size).  VEC: rows start 16-byte aligned and 8 logits move per lane and
-// step; otherwise one logit per lane and step.
-template <bool VEC, int UNROLL>
+// size).  This form, one wave per row and one logit per lane and step,
+// serves rows that are not 16-byte aligned.
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
 ce_rows_bf16_kernel(uint16_t* __restrict__ z, int64_t ldz, const int32_t* __restrict__ targets,
                     int rows, int V, float scale, float* __restrict__ row_loss,
@@ -501,25 +500,7 @@ ce_rows_bf16_kernel(uint16_t* __restrict__ z, int64_t ldz, const int32_t* __rest
   const float zt = t_ok ? __uint_as_float((uint32_t)zr[t] << 16) : __builtin_nanf("");
 
   float m = -INFINITY, s = 0.0f;
-  const int nvec = VEC ? V >> 3 : 0;
-  const u32x4* zv = reinterpret_cast<const u32x4*>(zr);
-  if constexpr (VEC) {
-    for (int v0 = 0; v0 < nvec; v0 += 64 * UNROLL) {
-      u32x4 x[UNROLL];
-#pragma unroll
-      for (int k = 0; k < UNROLL; ++k)
-        if (v0 + lane + 64 * k < nvec) x[k] = zv[v0 + lane + 64 * k];
-#pragma unroll
-      for (int k = 0; k < UNROLL; ++k) {
-        if (v0 + lane + 64 * k >= nvec) continue;
-        online_add4(f32x4{bf16_lo(x[k][0]), bf16_hi(x[k][0]), bf16_lo(x[k][1]),
-                          bf16_hi(x[k][1])}, m, s);
-        online_add4(f32x4{bf16_lo(x[k][2]), bf16_hi(x[k][2]), bf16_lo(x[k][3]),
-                          bf16_hi(x[k][3])}, m, s);
-      }
-    }
-  }
-  for (int j = 8 * nvec + lane; j < V; j += 64)
+  for (int j = lane; j < V; j += 64)
     online_add(to_log2(__uint_as_float((uint32_t)zr[j] << 16)), m, s);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -530,33 +511,98 @@ ce_rows_bf16_kernel(uint16_t* __restrict__ z, int64_t ldz, const int32_t* __rest
   const float lse2 = m + log2_hw(s);
   if (lane == 0)
     row_loss[(int64_t)row * loss_stride] = ((m - to_log2(zt)) + log2_hw(s)) * kLn2;
+  for (int j = lane; j < V; j += 64) {
+    const float p = exp2_hw(to_log2(__uint_as_float((uint32_t)zr[j] << 16)) - lse2);
+    zr[j] = (uint16_t)bf16_bits((p - (j == t ? 1.0f : 0.0f)) * scale);
+  }
+}
 
-  if constexpr (VEC) {
-    u32x4* zw = reinterpret_cast<u32x4*>(zr);
-    for (int v0 = 0; v0 < nvec; v0 += 64 * UNROLL) {
-      u32x4 x[UNROLL];
+// The same for rows that start 16-byte aligned, one 512-thread workgroup
+// per row: pass 1 spreads the row's 16-byte pieces over the workgroup's
+// threads, each thread's (max, sum) is combined over its wave with
+// shuffles and over the waves through LDS in a fixed order, and pass 2 has
+// every thread rewrite the pieces it read (after the barrier that ends
+// pass 1, so no thread writes before every read of the row is done).  Eight
+// waves per row keep enough requests in flight when a batch has few rows
+// (a single wave per row left a 1024-row batch with four waves per CU).
+constexpr int kRowBlockThreads = 512;
+constexpr int kRowBlockWaves = kRowBlockThreads / 64;
+
+template <int UNROLL>
+__global__ void __launch_bounds__(kRowBlockThreads)
+ce_rows_bf16_block_kernel(uint16_t* __restrict__ z, int64_t ldz,
+                          const int32_t* __restrict__ targets, int V, float scale,
+                          float* __restrict__ row_loss, int64_t loss_stride) {
+  __shared__ float wm[kRowBlockWaves], ws[kRowBlockWaves];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  uint16_t* zr = z + (int64_t)row * ldz;
+  const int t = targets[row];
+  const bool t_ok = (t >= 0) && (t < V);
+  const float zt = t_ok ? __uint_as_float((uint32_t)zr[t] << 16) : __builtin_nanf("");
+
+  float m = -INFINITY, s = 0.0f;
+  const int nvec = V >> 3;
+  const u32x4* zv = reinterpret_cast<const u32x4*>(zr);
+  for (int v0 = 0; v0 < nvec; v0 += kRowBlockThreads * UNROLL) {
+    u32x4 x[UNROLL];
 #pragma unroll
-      for (int k = 0; k < UNROLL; ++k)
-        if (v0 + lane + 64 * k < nvec) x[k] = zw[v0 + lane + 64 * k];
+    for (int k = 0; k < UNROLL; ++k)
+      if (v0 + tid + kRowBlockThreads * k < nvec) x[k] = zv[v0 + tid + kRowBlockThreads * k];
 #pragma unroll
-      for (int k = 0; k < UNROLL; ++k) {
-        const int v = v0 + lane + 64 * k;
-        if (v >= nvec) continue;
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 8 * v + 2 * e;
-          const float g0 =
-              (exp2_hw(to_log2(bf16_lo(x[k][e])) - lse2) - (j == t ? 1.0f : 0.0f)) * scale;
-          const float g1 =
-              (exp2_hw(to_log2(bf16_hi(x[k][e])) - lse2) - (j + 1 == t ? 1.0f : 0.0f)) * scale;
-          w[e] = pack_bf16x2(g0, g1);
-        }
-        zw[v] = w;
-      }
+    for (int k = 0; k < UNROLL; ++k) {
+      if (v0 + tid + kRowBlockThreads * k >= nvec) continue;
+      online_add4(f32x4{bf16_lo(x[k][0]), bf16_hi(x[k][0]), bf16_lo(x[k][1]), bf16_hi(x[k][1])},
+                  m, s);
+      online_add4(f32x4{bf16_lo(x[k][2]), bf16_hi(x[k][2]), bf16_lo(x[k][3]), bf16_hi(x[k][3])},
+                  m, s);
     }
   }
-  for (int j = 8 * nvec + lane; j < V; j += 64) {
+  for (int j = 8 * nvec + tid; j < V; j += kRowBlockThreads)
+    online_add(to_log2(__uint_as_float((uint32_t)zr[j] << 16)), m, s);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off, 64);
+    const float s2 = __shfl_xor(s, off, 64);
+    combine(m, s, m2, s2);
+  }
+  if (lane == 0) {
+    wm[tid >> 6] = m;
+    ws[tid >> 6] = s;
+  }
+  __syncthreads();
+  m = wm[0];
+  s = ws[0];
+#pragma unroll
+  for (int w = 1; w < kRowBlockWaves; ++w) combine(m, s, wm[w], ws[w]);
+  const float lse2 = m + log2_hw(s);
+  if (tid == 0) row_loss[(int64_t)row * loss_stride] = ((m - to_log2(zt)) + log2_hw(s)) * kLn2;
+
+  u32x4* zw = reinterpret_cast<u32x4*>(zr);
+  for (int v0 = 0; v0 < nvec; v0 += kRowBlockThreads * UNROLL) {
+    u32x4 x[UNROLL];
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k)
+      if (v0 + tid + kRowBlockThreads * k < nvec) x[k] = zw[v0 + tid + kRowBlockThreads * k];
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {
+      const int v = v0 + tid + kRowBlockThreads * k;
+      if (v >= nvec) continue;
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 8 * v + 2 * e;
+        const float g0 =
+            (exp2_hw(to_log2(bf16_lo(x[k][e])) - lse2) - (j == t ? 1.0f : 0.0f)) * scale;
+        const float g1 =
+            (exp2_hw(to_log2(bf16_hi(x[k][e])) - lse2) - (j + 1 == t ? 1.0f : 0.0f)) * scale;
+        w[e] = pack_bf16x2(g0, g1);
+      }
+      zw[v] = w;
+    }
+  }
+  for (int j = 8 * nvec + tid; j < V; j += kRowBlockThreads) {
     const float p = exp2_hw(to_log2(__uint_as_float((uint32_t)zr[j] << 16)) - lse2);
     zr[j] = (uint16_t)bf16_bits((p - (j == t ? 1.0f : 0.0f)) * scale);
   }
@@ -629,11 +675,11 @@ hipError_t launch_ce_rows_bf16(uint16_t* z, int64_t ldz, const int32_t* targets,
   const dim3 block(64 * kWavesPerBlock);
   const bool vec = ((ldz & 7) == 0) && ((reinterpret_cast<uintptr_t>(z) & 15) == 0);
   if (vec)
-    hipLaunchKernelGGL((ce_rows_bf16_kernel<true, 4>), grid, block, 0, s, z, ldz, targets, rows,
-                       V, scale, row_loss, loss_stride);
+    hipLaunchKernelGGL((ce_rows_bf16_block_kernel<4>), dim3(rows), dim3(kRowBlockThreads), 0, s,
+                       z, ldz, targets, V, scale, row_loss, loss_stride);
   else
-    hipLaunchKernelGGL((ce_rows_bf16_kernel<false, 4>), grid, block, 0, s, z, ldz, targets,
-                       rows, V, scale, row_loss, loss_stride);
+    hipLaunchKernelGGL(ce_rows_bf16_kernel, grid, block, 0, s, z, ldz, targets, rows, V, scale,
+                       row_loss, loss_stride);
   return hipGetLastError();
 }
 

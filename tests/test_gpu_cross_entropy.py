@@ -43,6 +43,8 @@ CASES = [  # rows, V, std, dtype, ld
     (4, 1, 1.0, torch.bfloat16, None),         # one class: loss 0, gradient 0
     (37, 1000, 3.0, torch.float32, None),
     (5, 40000, 30.0, torch.bfloat16, None),    # large spread: max-shifted sums
+    (12, 1003, 2.0, torch.bfloat16, 1008),     # aligned rows, 3 logits past the last 16 bytes
+    (40, 16, 1.0, torch.bfloat16, None),       # two 16-byte pieces a row
 ]
 
 
