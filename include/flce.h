@@ -211,10 +211,11 @@ flce_status flce_ce_rows(float* z, int64_t ldz, const int32_t* targets,
  *   z[i, j]   <- (softmax(z[i, :])_j - [j == t_i]) / rows, in place, same
  *               dtype and positions (bf16 rounded to nearest even)
  * i.e. the logits become dloss/dlogits of the mean loss.  Two passes over
- * each row (max / sum, then the rewrite), one wave64 per row; the mean is
- * summed in fp64 in a fixed order.  logits must be aligned to its element
- * size (16 bytes with ld % 8 == 0 for bf16, resp. ld % 4 == 0 for fp32,
- * selects the vector path); targets 0 <= t < V (an out-of-range target is
+ * each row (max / sum, then the rewrite): bf16 rows that start 16-byte
+ * aligned (ld % 8 == 0) take one 512-thread workgroup per row, other bf16
+ * rows and fp32 rows one wave64 per row; the mean is summed in fp64 in a
+ * fixed order.  logits must be aligned to its element size (fp32 rows
+ * 16-byte aligned with ld % 4 == 0 take a vector path); targets 0 <= t < V (an out-of-range target is
  * never dereferenced and makes the loss NaN).  Null pointers or bad sizes
  * give FLCE_ERR_INVALID_ARG, misalignment FLCE_ERR_UNSUPPORTED.
  */
