@@ -595,7 +595,7 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
             for (int t = 0; t < 16; ++t) {
               const float* src = corner + (lane_off + (uint32_t)t * row8 + 32u * i);
               if (!kGuard || (m_ok && n_lane + 8 * t < g.N))
-                old[t] = *reinterpret_cast<const f32x4*>(src);
+                old[t] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src));
               else
                 old[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             }
@@ -616,8 +616,16 @@ gemm_bf16_dma_kernel(GemmArgs g, int group_m) {
             f32x4 v = *reinterpret_cast<const f32x4*>(b + lds_off(nl, c_rd));
             if constexpr (kAcc) v += old[t];
             float* dst = corner + (lane_off + (uint32_t)t * row8 + 32u * i);
-            if (!kGuard || (m_ok && n_lane + 8 * t < g.N))
-              *reinterpret_cast<f32x4*>(dst) = v;
+            if (!kGuard || (m_ok && n_lane + 8 * t < g.N)) {
+              // The accumulated fp32 output is next read a whole chunk later
+              // (or by the caller): streamed past the caches, measured 1-2%
+              // faster for grad_W.  K-split parts, read back right away by
+              // the summing pass, stay cached.
+              if constexpr (EPI == kAccumF32)
+                __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+              else
+                *reinterpret_cast<f32x4*>(dst) = v;
+            }
           }
         }
       };
