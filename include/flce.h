@@ -148,17 +148,20 @@ flce_status flce_scale_grads(void* grad_h, int64_t n_h, float* grad_W, int64_t n
                              const float* scale, flce_dtype dt, hipStream_t stream);
 
 /*
- * Kernel launches flce_fwd_bwd makes for these sizes: FLCE_STEPS per token
- * chunk, i.e. FLCE_STEPS * ceil(N / min(chunk, N)).  0 if a size is < 1.
+ * Steps flce_fwd_bwd runs for these sizes: FLCE_STEPS per token chunk,
+ * i.e. FLCE_STEPS * ceil(N / min(chunk, N)).  0 if a size is < 1.  A step
+ * is one or two kernel launches (on the exponentiated bf16 path the row
+ * step is a statistics launch and a rewrite launch, and a K-split grad_h
+ * adds a summing launch).
  */
 #define FLCE_STEPS 5
 int64_t flce_launch_count(int64_t N, int64_t chunk);
 
 /*
  * flce_fwd_bwd that also records, on `stream`, events[2k] just before and
- * events[2k + 1] just after its k-th kernel launch, so a caller can time
- * each step with hipEventElapsedTime.  Launch k belongs to token chunk
- * k / FLCE_STEPS and is step k % FLCE_STEPS of that chunk: 0 logits GEMM,
+ * events[2k + 1] just after its k-th step, so a caller can time each step
+ * with hipEventElapsedTime.  Step k belongs to token chunk k / FLCE_STEPS
+ * and is step k % FLCE_STEPS of that chunk: 0 logits GEMM,
  * 1 row log-sum-exp + gradient rewrite, 2 loss sum, 3 grad_h GEMM,
  * 4 grad_W GEMM.  `events` is a HOST array of n_events handles the caller
  * created (hipEventCreate) and owns; n_events must be at least

@@ -147,7 +147,7 @@ extern "C" int64_t flce_launch_count(int64_t N, int64_t chunk) {
 
 namespace {
 
-// Records events[2k] / events[2k+1] around launch k when events != nullptr.
+// Records events[2k] / events[2k+1] around step k when events != nullptr.
 struct Marks {
   hipEvent_t* ev;
   hipStream_t s;
