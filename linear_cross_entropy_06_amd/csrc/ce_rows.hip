@@ -238,8 +238,24 @@ __device__ __forceinline__ void combine_pairs(const float* pr, int nq, int q_ski
                                               float& m, float& a) {
   m = -INFINITY;
   a = 0.0f;
-  for (int q = lane; q < nq; q += 64)
-    if (q != q_skip) combine(m, a, pr[2 * q], pr[2 * q + 1]);
+  // Eight pairs per lane are requested before any is combined (the
+  // statistics kernel is bound by these round trips); the combining order
+  // is the plain one, q = lane, lane + 64, ...
+  constexpr int kBatch = 8;
+  for (int q0 = lane; q0 < nq; q0 += 64 * kBatch) {
+    float pm[kBatch], ps[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int q = q0 + 64 * k;
+      pm[k] = q < nq ? pr[2 * q] : -INFINITY;
+      ps[k] = q < nq ? pr[2 * q + 1] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int q = q0 + 64 * k;
+      if (q < nq && q != q_skip) combine(m, a, pm[k], ps[k]);
+    }
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float m2 = __shfl_xor(m, off, 64);
@@ -297,11 +313,27 @@ __device__ __forceinline__ float target_logit(const uint16_t* h_row, const uint1
   const u32x4* hv = reinterpret_cast<const u32x4*>(h_row);
   const u32x4* wv = reinterpret_cast<const u32x4*>(w_row);
   float acc = 0.0f;
-  for (int k = lane; k < H / 8; k += 64) {
-    const u32x4 a = hv[k], b = wv[k];
+  // Four pieces of each row requested at a time; accumulated in the plain
+  // order k = lane, lane + 64, ...
+  constexpr int kBatch = 4;
+  const int n8 = H / 8;
+  for (int k0 = lane; k0 < n8; k0 += 64 * kBatch) {
+    u32x4 a[kBatch], b[kBatch];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc += bf16_lo(a[e]) * bf16_lo(b[e]) + bf16_hi(a[e]) * bf16_hi(b[e]);
+    for (int j = 0; j < kBatch; ++j) {
+      const int k = k0 + 64 * j;
+      if (k < n8) {
+        a[j] = hv[k];
+        b[j] = wv[k];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (k0 + 64 * j >= n8) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc += bf16_lo(a[j][e]) * bf16_lo(b[j][e]) + bf16_hi(a[j][e]) * bf16_hi(b[j][e]);
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
